@@ -1,0 +1,75 @@
+"""Seeded synthetic inputs for the skinny residual GEMM.
+
+This module only draws and lays out input tensors; it holds none of the
+operation's arithmetic. Both the GPU tests/benchmark and the CPU oracle's
+callers take their inputs from here, so both sides see the same bytes.
+
+Recipe (shapes and seed base follow the vLLM benchmark page
+"benchmarks/kernels/benchmark_k3_cutedsl_residual.py", its ``main``):
+  * one CPU ``torch.Generator`` seeded with ``20260722 + M``;
+  * draw order: X, then W copies 0..C-1, then R copies 0..C-1;
+  * X ~ N(0,1), R ~ N(0,1), W ~ N(0,1)/sqrt(K), each drawn in fp32 and rounded
+    to bf16 by torch's conversion (round-to-nearest-even).
+The page draws W unscaled; the 1/sqrt(K) factor keeps the product term at unit
+scale so that neither the product nor the residual dominates the output.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+SEED_BASE = 20260722
+N_DEFAULT = 7168
+K_DEFAULT = 3584
+
+
+def generator(M: int, seed: int | None = None) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(SEED_BASE + M if seed is None else seed)
+    return g
+
+
+def make_inputs(M: int, N: int = N_DEFAULT, K: int = K_DEFAULT, copies: int = 1,
+                seed: int | None = None):
+    """Return (X, [W_0..W_{C-1}], [R_0..R_{C-1}]) as CPU bf16 tensors."""
+    g = generator(M, seed)
+    X = torch.randn((M, K), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    ws = []
+    scale = 1.0 / math.sqrt(K) if K > 0 else 1.0
+    for _ in range(copies):
+        ws.append((torch.randn((N, K), generator=g, dtype=torch.float32) * scale).to(torch.bfloat16))
+    rs = [torch.randn((M, N), generator=g, dtype=torch.float32).to(torch.bfloat16) for _ in range(copies)]
+    return X, ws, rs
+
+
+def bits(t: torch.Tensor):
+    """bf16 tensor -> numpy uint16 bit patterns (a copy on the host)."""
+    import numpy as np
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def from_bits(b) -> torch.Tensor:
+    """numpy uint16 bit patterns -> CPU bf16 tensor."""
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+# ---- structured inputs for exact cases (no arithmetic of the operation) -------------
+
+def one_hot_rows(N: int, K: int, cols) -> torch.Tensor:
+    """W with row n equal to the unit vector e_{cols[n]} (bf16 1.0 at one position)."""
+    W = torch.zeros((N, K), dtype=torch.bfloat16)
+    W[torch.arange(N), torch.as_tensor(cols, dtype=torch.long)] = 1.0
+    return W
+
+
+def small_int_inputs(M: int, N: int, K: int, seed: int = 7):
+    """Integer-valued X in [-2,2], W[n,k] = ((n + 3k) mod 5) - 2, R in [-8,8]."""
+    g = generator(M, seed)
+    X = torch.randint(-2, 3, (M, K), generator=g).to(torch.bfloat16)
+    n = torch.arange(N).view(N, 1)
+    k = torch.arange(K).view(1, K)
+    W = (((n + 3 * k) % 5) - 2).to(torch.bfloat16)
+    R = torch.randint(-8, 9, (M, N), generator=g).to(torch.bfloat16)
+    return X, W, R

@@ -1,0 +1,155 @@
+"""TEST INFRASTRUCTURE ONLY -- the CPU oracle for Y = X * W^T + R.
+
+Plain fp64 definition of the skinny residual GEMM (bf16 X[M,K], W[N,K],
+R[M,N]; one round-to-nearest-even to bf16), written from the vLLM benchmark
+page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py" (module docstring
+and its torch.addmm leg). The arithmetic lives in ``oracle.c``; this module
+only builds it with gcc and marshals numpy arrays.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU library
+and imports nothing from it.
+
+Arrays of bf16 are passed as ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_default = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c into a shared library (plain gcc: no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(out):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-pthread", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _u16(a, shape=None) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 operands are passed as uint16 bit patterns, got %s" % a.dtype)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+class Oracle:
+    """ctypes view of one build of oracle.c (the default build, or a test's own build)."""
+
+    def __init__(self, path: str = _LIB):
+        lib = ctypes.CDLL(path)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.oracle_addmm_bf16.argtypes = [u16p, u16p, u16p, u16p, f64p, i64, i64, i64, ctypes.c_int]
+        lib.oracle_addmm_bf16.restype = ctypes.c_int
+        lib.oracle_addmm_bf16_points.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64p, i64p, i64,
+                                                 u16p, f64p]
+        lib.oracle_addmm_bf16_points.restype = ctypes.c_int
+        lib.oracle_round_bf16_array.argtypes = [f64p, u16p, i64]
+        lib.oracle_round_bf16_array.restype = None
+        self.lib = lib
+        self.path = path
+
+    def addmm_bf16(self, X, W, R, threads: int | None = None, want_acc: bool = True):
+        """Return (Y bits uint16[M,N], exact fp64 sums float64[M,N] or None)."""
+        X = _u16(X)
+        W = _u16(W)
+        if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
+            raise ValueError("X must be [M,K] and W [N,K]")
+        M, K = X.shape
+        N = W.shape[0]
+        R = _u16(R, (M, N))
+        Y = np.empty((M, N), dtype=np.uint16)
+        ACC = np.empty((M, N), dtype=np.float64) if want_acc else None
+        rc = self.lib.oracle_addmm_bf16(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
+                                        _ptr(R, ctypes.c_uint16), _ptr(Y, ctypes.c_uint16),
+                                        _ptr(ACC, ctypes.c_double) if ACC is not None else None,
+                                        M, N, K, int(threads or default_threads()))
+        if rc != 0:
+            raise RuntimeError("oracle_addmm_bf16 failed (%d)" % rc)
+        return Y, ACC
+
+    def addmm_bf16_points(self, X, W, R, ms, ns):
+        """Oracle values at the listed (m, n): (Y bits uint16[c], fp64 sums float64[c])."""
+        X = _u16(X)
+        W = _u16(W)
+        M, K = X.shape
+        N = W.shape[0]
+        R = _u16(R, (M, N))
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        if ms.shape != ns.shape or ms.ndim != 1:
+            raise ValueError("ms and ns must be 1-D and of equal length")
+        c = ms.shape[0]
+        Y = np.empty(c, dtype=np.uint16)
+        ACC = np.empty(c, dtype=np.float64)
+        rc = self.lib.oracle_addmm_bf16_points(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
+                                               _ptr(R, ctypes.c_uint16), M, N, K,
+                                               _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64), c,
+                                               _ptr(Y, ctypes.c_uint16), _ptr(ACC, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("point index out of range")
+        return Y, ACC
+
+    def round_bf16(self, v) -> np.ndarray:
+        """The oracle's rounding step, elementwise: float64 -> bf16 bits."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.oracle_round_bf16_array(_ptr(v, ctypes.c_double), _ptr(out, ctypes.c_uint16), v.size)
+        return out
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def addmm_bf16(X, W, R, threads: int | None = None, want_acc: bool = True):
+    return default().addmm_bf16(X, W, R, threads=threads, want_acc=want_acc)
+
+
+def addmm_bf16_points(X, W, R, ms, ns):
+    return default().addmm_bf16_points(X, W, R, ms, ns)
+
+
+def round_bf16(v) -> np.ndarray:
+    return default().round_bf16(v)
+
+
+def source_path() -> str:
+    return _SRC
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float64 (bits << 16 read as binary32)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
