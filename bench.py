@@ -1,0 +1,416 @@
+#!/usr/bin/env python3
+"""Benchmark of the skinny residual GEMM  Y = bf16(X W^T + R)  on one MI355X.
+
+Method (the vLLM benchmark page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py",
+functions graph_samples / summarize / rotating_buffer_count, re-done for HIP):
+  * seeded synthetic inputs (decode_skinny_addmm_amd.synth), N = 7168, K = 3584;
+  * W and R rotate over C copies (default 6, about 308 MB: more than the 256 MB Infinity
+    Cache and the L2s), so every call streams its W from HBM;
+  * one HIP graph captures `--calls` launches (default 500) cycling over the copies;
+    a step is one replay of that graph; warm-up replays are untimed;
+  * HIP events on the stream the graph runs on bracket every timed replay.
+
+Default run (no flags): M = 4, 6 copies, 500 calls per graph, prints ONE JSON line with
+the throughput (algorithmic HBM GB/s), the roofline fraction against 8 TB/s and the CPU
+oracle timed on this host as a baseline.
+
+Other modes write JSONL rows (one per configuration or M) to --out:
+  --mode sweep    every built configuration at --m (default 16)
+  --mode mcurve   M in {1,2,4,8,16,32,64,128,256}, library-selected configuration
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+N_DIM = 7168
+K_DIM = 3584
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (published)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+
+
+def algorithmic_bytes(M: int, N: int = N_DIM, K: int = K_DIM) -> int:
+    """W read once, X read once, R read once, Y written once (bf16)."""
+    return 2 * N * K + 2 * M * K + 2 * M * N + 2 * M * N
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_config(s: str | None):
+    if not s:
+        return None
+    v = [int(t) for t in s.split(",")]
+    if len(v) not in (5, 6, 7):
+        raise argparse.ArgumentTypeError("config must be PATH,BLOCK,OUTPUTS,K_UNROLL,VECTOR_WIDTH[,M_TILE[,K_SPLIT]]")
+    keys = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
+    d = dict(zip(keys, v))
+    d.setdefault("m_tile", 0)
+    d.setdefault("k_split", 1)
+    return d
+
+
+def percentile(ordered, frac):
+    pos = frac * (len(ordered) - 1)
+    lo, hi = math.floor(pos), math.ceil(pos)
+    if lo == hi:
+        return ordered[lo]
+    w = pos - lo
+    return ordered[lo] * (1 - w) + ordered[hi] * w
+
+
+def summarize(samples):
+    o = sorted(samples)
+    mean = statistics.mean(samples)
+    return {"median_us": statistics.median(samples), "p10_us": percentile(o, 0.1),
+            "p90_us": percentile(o, 0.9), "mean_us": mean,
+            "cv_pct": statistics.pstdev(samples) / mean * 100.0 if mean else 0.0}
+
+
+class Workload:
+    """Device-resident inputs: one X, C copies of W and R, C outputs."""
+
+    def __init__(self, M: int, copies: int, N: int = N_DIM, K: int = K_DIM):
+        import torch
+
+        from decode_skinny_addmm_amd import synth
+        t0 = time.time()
+        X, ws, rs = synth.make_inputs(M, N, K, copies=copies)
+        self.host = (X, ws[0], rs[0])
+        self.M, self.N, self.K, self.copies = M, N, K, copies
+        self.X = X.cuda()
+        self.W = [w.cuda() for w in ws]
+        self.R = [r.cuda() for r in rs]
+        self.Y = [torch.empty_like(r) for r in self.R]
+        del ws, rs
+        torch.cuda.synchronize()
+        log("inputs M=%d copies=%d ready in %.1fs (%.1f MB of W+R)" % (
+            M, copies, time.time() - t0, copies * (N * K + M * N) * 2 / 1e6))
+
+
+def time_graph(launch, wl, calls: int, warmup: int, steps: int):
+    """Capture `calls` launches cycling over the copies into one graph; time `steps` replays.
+
+    Returns (per-replay microseconds list, total elapsed ms, stream used)."""
+    import torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(wl.copies):  # eager warm-up over every copy
+            launch(wl.X, wl.W[i], wl.R[i], wl.Y[i])
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in range(calls):
+            i = c % wl.copies
+            launch(wl.X, wl.W[i], wl.R[i], wl.Y[i])
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+    stream.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        events[0].record(stream)
+        for s in range(steps):
+            g.replay()
+            events[s + 1].record(stream)
+    events[-1].synchronize()
+    torch.cuda.synchronize()
+    per = [events[s].elapsed_time(events[s + 1]) * 1000.0 for s in range(steps)]  # us per replay
+    total_ms = events[0].elapsed_time(events[-1])
+    del g
+    return per, total_ms
+
+
+def secondary_correctness(wl, launch):
+    """Page-1 style statistics of copy 0 against an fp32 torch product (reported, not gating)."""
+    import torch
+    X, W, R = wl.X, wl.W[0], wl.R[0]
+    Y = torch.empty_like(R)
+    launch(X, W, R, Y)
+    torch.cuda.synchronize()
+    ref = X.float() @ W.float().t() + R.float()
+    err = (Y.float() - ref).abs()
+    cos = torch.nn.functional.cosine_similarity(Y.float().flatten(), ref.flatten(), dim=0).item()
+    return {"cosine": cos, "max_abs_error": err.max().item(),
+            "max_scaled_error": (err / (ref.abs() + 1.0)).max().item(), "valid": cos > 0.999}
+
+
+def oracle_parity_sample(wl, launch, count=512):
+    """Sampled oracle check of copy 0 (2 bf16 ULP rule); returns the max ULP distance."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from decode_skinny_addmm_amd import synth
+    X, W, R = wl.host
+    Y = torch.empty_like(wl.R[0])
+    launch(wl.X, wl.W[0], wl.R[0], Y)
+    torch.cuda.synchronize()
+    yg = synth.bits(Y)
+    rng = np.random.default_rng(0)
+    ms = rng.integers(0, wl.M, count)
+    ns = rng.integers(0, wl.N, count)
+    yo, ex = oracle.addmm_bf16_points(synth.bits(X), synth.bits(W), synth.bits(R), ms, ns)
+
+    def key(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    d = np.abs(key(yg[ms, ns]) - key(yo))
+    big = np.abs(ex) >= 2.0 ** -12
+    return int(d[big].max()) if big.any() else 0
+
+
+def cpu_baseline(M: int, seconds: float):
+    """The CPU oracle, as it stands, on full calls of the same workload (copy 0)."""
+    import oracle
+    from decode_skinny_addmm_amd import synth
+    X, ws, rs = synth.make_inputs(M, N_DIM, K_DIM)
+    Xb, Wb, Rb = synth.bits(X), synth.bits(ws[0]), synth.bits(rs[0])
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        threads = min(threads, int(omp))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.addmm_bf16(Xb, Wb, Rb, threads=threads, want_acc=False)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_call = el / calls
+    return {"value": algorithmic_bytes(M) / per_call / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "us_per_call": per_call * 1e6,
+            "sample": "%d full calls (M=%d, N=%d, K=%d, copy 0) in %.1f s on %d threads" % (
+                calls, M, N_DIM, K_DIM, el, threads)}
+
+
+def probe_launches(sk):
+    """Reference kernels (include/skinny_probe.h) with the operation's launch signature."""
+    import torch
+    L = sk.ops.lib()
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def null(X, W, R, Y):
+        sk.ops.check(L.skinny_probe_null(cur()), "skinny_probe_null")
+
+    def read(X, W, R, Y, unroll=8):
+        sk.ops.check(L.skinny_probe_read(W.data_ptr(), W.numel() * 2, sink.data_ptr(), 0, unroll, cur()),
+                     "skinny_probe_read")
+    return null, read
+
+
+def reference_rows(sk, wl, calls, warmup, steps):
+    """Per-launch floor and the streaming-read rate over the same rotating W copies."""
+    null, read = probe_launches(sk)
+    out = {}
+    per, total_ms = time_graph(null, wl, calls, warmup, steps)
+    out["null_kernel_us"] = total_ms * 1000.0 / (steps * calls)
+    for u in (4, 8, 16):
+        per, total_ms = time_graph(lambda X, W, R, Y, u=u: read(X, W, R, Y, u), wl, calls, warmup, steps)
+        us = total_ms * 1000.0 / (steps * calls)
+        out["stream_read_u%d" % u] = {"us": us, "gbs": wl.N * wl.K * 2 / (us * 1e-6) / 1e9}
+    best = max(v["gbs"] for k, v in out.items() if k.startswith("stream_read"))
+    out["stream_read_best_gbs"] = best
+    return out
+
+
+def run_probe(args, sk):
+    """Streaming-read reference kernel over launch shapes (JSONL rows to --out)."""
+    import torch
+    null, read = probe_launches(sk)
+    L = sk.ops.lib()
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    wl = Workload(1, args.copies)
+    out = open(args.out, "a") if args.out else None
+    nbytes = wl.N * wl.K * 2
+    shapes = []
+    for u in (1, 2, 4, 8, 16):
+        for blocks in (256, 512, 1024, 2048, 4096, 8192):
+            shapes.append((blocks, u))
+        shapes.append((nbytes // (4096 * u), u))  # one pass: every thread one batch of u loads
+    for blocks, u in shapes:
+        def launch(X, W, R, Y, b=blocks, u=u):
+            sk.ops.check(L.skinny_probe_read(W.data_ptr(), nbytes, sink.data_ptr(), b, u,
+                                             torch.cuda.current_stream().cuda_stream), "probe_read")
+        per, total_ms = time_graph(launch, wl, args.calls, args.warmup, args.steps)
+        us = total_ms * 1000.0 / (args.steps * args.calls)
+        row = {"probe": "read", "bytes": nbytes, "blocks": blocks, "unroll": u, "us": us,
+               "gbs": nbytes / (us * 1e-6) / 1e9}
+        log(json.dumps(row))
+        if out:
+            out.write(json.dumps(row) + "\n")
+    # steady state: one launch over all copies at once (one large buffer)
+    big = torch.empty(wl.copies * nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    for u in (2, 4, 8):
+        for blocks in (1024, 2048, 4096):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for rep in range(3):
+                sk.ops.check(L.skinny_probe_read(big.data_ptr(), big.numel() * 2, sink.data_ptr(), blocks, u,
+                                                 torch.cuda.current_stream().cuda_stream), "probe_read")
+            torch.cuda.synchronize()
+            ev[0].record()
+            for rep in range(20):
+                sk.ops.check(L.skinny_probe_read(big.data_ptr(), big.numel() * 2, sink.data_ptr(), blocks, u,
+                                                 torch.cuda.current_stream().cuda_stream), "probe_read")
+            ev[1].record()
+            ev[1].synchronize()
+            us = ev[0].elapsed_time(ev[1]) * 1000.0 / 20
+            row = {"probe": "read_big", "bytes": big.numel() * 2, "blocks": blocks, "unroll": u, "us": us,
+                   "gbs": big.numel() * 2 / (us * 1e-6) / 1e9}
+            log(json.dumps(row))
+            if out:
+                out.write(json.dumps(row) + "\n")
+    if out:
+        out.close()
+
+
+def make_launch(sk, config):
+    if config is None:
+        return lambda X, W, R, Y: sk.addmm_default(X, W, R, Y)
+    return lambda X, W, R, Y: sk.addmm(X, W, R, out=Y, config=config)
+
+
+def measure(sk, wl, config, calls, warmup, steps):
+    launch = make_launch(sk, config)
+    per, total_ms = time_graph(launch, wl, calls, warmup, steps)
+    us_per_call = [p / calls for p in per]
+    mean_us = total_ms * 1000.0 / (steps * calls)
+    gbs = algorithmic_bytes(wl.M) / (mean_us * 1e-6) / 1e9
+    return launch, us_per_call, mean_us, gbs
+
+
+def run_default(args, sk):
+    import torch
+    M = args.m
+    wl = Workload(M, args.copies)
+    cfg = args.config or sk.select_config(M)
+    launch, samples, mean_us, gbs = measure(sk, wl, cfg, args.calls, args.warmup, args.steps)
+    st = summarize(samples)
+    flops = 2.0 * M * N_DIM * K_DIM
+    res = sk.config_resources(cfg) if cfg.get("m_tile") else None
+    row = {
+        "metric": "us/call + achieved HBM GB/s (% roofline), Y=X*W^T+R N=7168 K=3584, M=1..256",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_us * args.calls / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "skinny residual GEMM M=%d N=%d K=%d, bf16 in/out, fp32 accumulate; "
+                               "W,R rotated over %d seeded copies; HIP graph of %d calls per step"
+                               % (M, N_DIM, K_DIM, args.copies, args.calls),
+                   "M": M, "N": N_DIM, "K": K_DIM, "copies": args.copies, "calls_per_step": args.calls,
+                   "kernel_config": cfg, "resources": res},
+        "us_per_call": round(mean_us, 4),
+        "us_per_call_stats": {k: round(v, 4) for k, v in st.items()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": algorithmic_bytes(M),
+                     "mfma_frac": round(flops / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_reference:
+        ref = reference_rows(sk, wl, args.calls, max(2, args.warmup // 4), max(5, args.steps // 5))
+        ref["op_frac_of_stream_read"] = round(gbs / ref["stream_read_best_gbs"], 4)
+        row["reference"] = ref
+    try:
+        row["parity_max_ulp_sampled"] = oracle_parity_sample(wl, launch)
+        row["secondary_correctness"] = secondary_correctness(wl, launch)
+    except Exception as e:  # noqa: BLE001
+        row["parity_error"] = "%s: %s" % (type(e).__name__, e)
+    if not args.no_cpu_baseline:
+        row["cpu_baseline"] = cpu_baseline(M, args.cpu_seconds)
+    print(json.dumps(row), flush=True)
+
+
+def sweep_rows(args, sk, Ms, config_lists):
+    import torch
+    out = open(args.out, "a") if args.out else None
+    meta = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip}
+    for M in Ms:
+        wl = Workload(M, args.copies)
+        for cfg in config_lists(M):
+            row = {"m": M, "n": N_DIM, "k": K_DIM, "config": cfg, "copies": args.copies,
+                   "calls": args.calls, **meta}
+            try:
+                launch, samples, mean_us, gbs = measure(sk, wl, cfg, args.calls, args.warmup, args.steps)
+                row.update(summarize(samples))
+                row.update({"mean_us_total": mean_us, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                            "resources": sk.config_resources(cfg) if cfg.get("m_tile") else None,
+                            "max_ulp_sampled": oracle_parity_sample(wl, launch, 256)})
+            except Exception as e:  # noqa: BLE001
+                row.update({"valid": False, "error": "%s: %s" % (type(e).__name__, e)})
+            line = json.dumps(row, sort_keys=True)
+            log(line)
+            if out:
+                out.write(line + "\n")
+                out.flush()
+        del wl
+        torch.cuda.empty_cache()
+    if out:
+        out.close()
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100, help="timed graph replays")
+    p.add_argument("--warmup", type=int, default=20, help="untimed graph replays")
+    p.add_argument("--m", type=int, default=None)
+    p.add_argument("--copies", type=int, default=6)
+    p.add_argument("--calls", type=int, default=500, help="launches captured per graph (one step)")
+    p.add_argument("--config", type=parse_config, default=None)
+    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe"), default="default")
+    p.add_argument("--out", type=str, default=None)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")
+    p.add_argument("--ms", type=str, default=None, help="comma-separated M list for sweep/mcurve")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import decode_skinny_addmm_amd as sk
+    sk.ops.lib()
+    if args.mode == "default":
+        args.m = args.m or 4
+        run_default(args, sk)
+    elif args.mode == "probe":
+        run_probe(args, sk)
+    elif args.mode == "sweep":
+        Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
+        sweep_rows(args, sk, Ms, lambda m: [c for c in sk.configs()])
+    else:
+        Ms = [int(x) for x in args.ms.split(",")] if args.ms else (
+            [args.m] if args.m else [1, 2, 4, 8, 16, 32, 64, 128, 256])
+        sweep_rows(args, sk, Ms, lambda m: [args.config or sk.select_config(m)])
+
+
+if __name__ == "__main__":
+    main()

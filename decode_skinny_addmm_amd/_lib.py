@@ -1,0 +1,87 @@
+"""ctypes declarations of libskinny.so (the C ABI in include/skinny.h). No arithmetic here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libskinny.so")
+
+STATUS = {0: "SKINNY_OK", 1: "SKINNY_EINVAL", 2: "SKINNY_EALIGN", 3: "SKINNY_ENOTSUP", 4: "SKINNY_EHIP"}
+PATH_GEMV = 0
+PATH_MFMA = 1
+CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
+
+EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
+            "skinny_addmm_bf16_acc_f32", "skinny_num_configs", "skinny_get_config",
+            "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
+            "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy")
+
+
+class SkinnyConfig(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in CONFIG_FIELDS]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f in CONFIG_FIELDS}
+
+
+class SkinnyResources(ctypes.Structure):
+    _fields_ = [("num_vgprs", ctypes.c_int32), ("spill_bytes", ctypes.c_int32),
+                ("lds_bytes_static", ctypes.c_int32), ("max_threads", ctypes.c_int32)]
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, status), _status_text(status)))
+
+
+_lib = None
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().skinny_status_string(status).decode()
+    except Exception:  # noqa: BLE001
+        return "?"
+
+
+def lib() -> ctypes.CDLL:
+    """Load libskinny.so; raise if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libskinny.so is not built (%s); run `python -m decode_skinny_addmm_amd.build` "
+                           "or __graft_entry__.build()" % LIB_PATH)
+    # Load torch first so the library binds to the HIP runtime torch already uses
+    # (same soname), and device pointers/streams from torch are valid for it.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    cfgp = ctypes.POINTER(SkinnyConfig)
+    L.skinny_addmm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    L.skinny_addmm_bf16_with_config.argtypes = [vp, vp, vp, vp, i64, i64, i64, cfgp, vp]
+    L.skinny_addmm_bf16_acc_f32.argtypes = [vp, vp, vp, vp, i64, i64, i64, cfgp, vp]
+    L.skinny_select_config.argtypes = [i64, i64, i64, cfgp]
+    L.skinny_get_config.argtypes = [ctypes.c_int32, cfgp]
+    L.skinny_config_resources.argtypes = [cfgp, ctypes.POINTER(SkinnyResources)]
+    L.skinny_status_string.argtypes = [ctypes.c_int]
+    L.skinny_status_string.restype = ctypes.c_char_p
+    L.skinny_version.restype = ctypes.c_char_p
+    L.skinny_probe_null.argtypes = [vp]
+    L.skinny_probe_read.argtypes = [vp, i64, vp, ctypes.c_int32, ctypes.c_int32, vp]
+    L.skinny_probe_copy.argtypes = [vp, vp, i64, vp]
+    for f in ("skinny_probe_null", "skinny_probe_read", "skinny_probe_copy"):
+        getattr(L, f).restype = ctypes.c_int
+    for f in ("skinny_addmm_bf16", "skinny_addmm_bf16_with_config", "skinny_addmm_bf16_acc_f32",
+              "skinny_select_config", "skinny_get_config", "skinny_config_resources",
+              "skinny_num_configs", "skinny_last_hip_error"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(status: int, what: str) -> None:
+    if status != 0:
+        raise SkinnyError(status, what)

@@ -1,0 +1,182 @@
+// api.hip -- the C ABI of libskinny.so (declared in include/skinny.h): argument checks,
+// configuration lookup and dispatch to the compiled kernel instances.
+#include <string.h>
+
+#include <climits>
+#include <vector>
+
+#include "common.hpp"
+
+namespace skinny {
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+#include "config_table.inc"
+
+struct Registry {
+    std::vector<const KernelEntry *> all;
+    Registry() {
+        int n = 0;
+        const KernelEntry *g = gemv_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&g[i]);
+        const KernelEntry *f = mfma_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&f[i]);
+    }
+};
+
+const Registry &registry() {
+    static const Registry r;
+    return r;
+}
+
+bool same_shape(const skinny_config &a, const skinny_config &b) {
+    return a.path == b.path && a.block_size == b.block_size &&
+           a.outputs_per_block == b.outputs_per_block && a.k_unroll == b.k_unroll &&
+           a.vector_width == b.vector_width && a.k_split == b.k_split;
+}
+
+// Exact match; with m_tile == 0 the smallest built m_tile >= M (else the largest) is used.
+const KernelEntry *find_entry(const skinny_config &c, int64_t M) {
+    const KernelEntry *best = nullptr;
+    for (const KernelEntry *e : registry().all) {
+        if (!same_shape(e->cfg, c)) continue;
+        if (c.m_tile != 0) {
+            if (e->cfg.m_tile == c.m_tile) return e;
+            continue;
+        }
+        if (!best) {
+            best = e;
+            continue;
+        }
+        const bool e_fits = e->cfg.m_tile >= M, b_fits = best->cfg.m_tile >= M;
+        if (e_fits && (!b_fits || e->cfg.m_tile < best->cfg.m_tile)) best = e;
+        else if (!e_fits && !b_fits && e->cfg.m_tile > best->cfg.m_tile) best = e;
+    }
+    return best;
+}
+
+skinny_config table_row(int64_t M) {
+    const int n = (int)(sizeof(kTable) / sizeof(kTable[0]));
+    for (int i = 0; i < n; ++i)
+        if (M <= kTable[i].max_m) return kTable[i].cfg;
+    return kTable[n - 1].cfg;
+}
+
+// The table's choice for M, unless that kernel cannot take this K (GEMV instances hold
+// their K slice in registers); then the general MFMA configuration, which loops over K.
+skinny_config select(int64_t M, int64_t K) {
+    const skinny_config c = table_row(M);
+    const KernelEntry *e = find_entry(c, M);
+    if (e && K <= e->max_k()) return c;
+    return M <= 16 ? kFallbackSmall : kFallbackLarge;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+skinny_status run(const void *X, const void *W, const void *R, void *out, bool acc_out,
+                  int64_t M, int64_t N, int64_t K, const skinny_config *cfg, void *stream) {
+    if (M < 0 || N < 0 || K < 0) return SKINNY_EINVAL;
+    if (K % 8 != 0) return SKINNY_ENOTSUP;
+    if (M == 0 || N == 0) return SKINNY_OK;
+    if (!R || !out) return SKINNY_EINVAL;
+    if (K > 0 && (!X || !W)) return SKINNY_EINVAL;
+    if ((X && !aligned(X, 16)) || (W && !aligned(W, 16)) || !aligned(R, 2) ||
+        !aligned(out, acc_out ? 4 : 2))
+        return SKINNY_EALIGN;
+    // kernel index arithmetic is 32-bit for sizes, 64-bit for offsets
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return SKINNY_ENOTSUP;
+    const skinny_config c = cfg ? *cfg : select(M, K);
+    if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
+        c.k_unroll <= 0 || (c.vector_width != 4 && c.vector_width != 8) || c.m_tile < 0 ||
+        c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0)
+        return SKINNY_EINVAL;
+    const KernelEntry *e = find_entry(c, M);
+    if (!e) return SKINNY_ENOTSUP;
+    if (K > e->max_k()) return SKINNY_ENOTSUP;
+    // K == 0 (Y = R): the GEMV kernels load their K slice unconditionally, so the empty
+    // sum goes to the general kernel, whose K loop simply does not run.
+    if (K == 0 && e->cfg.path == SKINNY_PATH_GEMV) e = find_entry(kFallbackSmall, M);
+    if (!e) return SKINNY_ENOTSUP;
+    const int64_t mt = e->cfg.m_tile;
+    if ((M + mt - 1) / mt > 65535) return SKINNY_ENOTSUP;
+    LaunchArgs a{static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(W),
+                 static_cast<const uint16_t *>(R), out, M, N, K, acc_out,
+                 static_cast<hipStream_t>(stream)};
+    const hipError_t err = e->launch(a);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return SKINNY_EHIP;
+    }
+    return SKINNY_OK;
+}
+
+}  // namespace
+}  // namespace skinny
+
+extern "C" {
+
+skinny_status skinny_addmm_bf16(const void *X, const void *W, const void *R, void *Y, int64_t M,
+                                int64_t N, int64_t K, void *stream) {
+    return skinny::run(X, W, R, Y, false, M, N, K, nullptr, stream);
+}
+
+skinny_status skinny_addmm_bf16_with_config(const void *X, const void *W, const void *R, void *Y,
+                                            int64_t M, int64_t N, int64_t K,
+                                            const skinny_config *cfg, void *stream) {
+    return skinny::run(X, W, R, Y, false, M, N, K, cfg, stream);
+}
+
+skinny_status skinny_addmm_bf16_acc_f32(const void *X, const void *W, const void *R, float *ACC,
+                                        int64_t M, int64_t N, int64_t K,
+                                        const skinny_config *cfg, void *stream) {
+    return skinny::run(X, W, R, ACC, true, M, N, K, cfg, stream);
+}
+
+skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out) {
+    if (!out || M < 0 || N < 0 || K < 0) return SKINNY_EINVAL;
+    *out = skinny::select(M, K);
+    return SKINNY_OK;
+}
+
+int32_t skinny_num_configs(void) { return (int32_t)skinny::registry().all.size(); }
+
+skinny_status skinny_get_config(int32_t index, skinny_config *out) {
+    if (!out || index < 0 || index >= skinny_num_configs()) return SKINNY_EINVAL;
+    *out = skinny::registry().all[(size_t)index]->cfg;
+    return SKINNY_OK;
+}
+
+skinny_status skinny_config_resources(const skinny_config *cfg, skinny_resources *out) {
+    if (!cfg || !out) return SKINNY_EINVAL;
+    const skinny::KernelEntry *e = skinny::find_entry(*cfg, cfg->m_tile > 0 ? cfg->m_tile : 1);
+    if (!e) return SKINNY_ENOTSUP;
+    hipFuncAttributes attr;
+    const hipError_t err = hipFuncGetAttributes(&attr, e->fn_bf16);
+    if (err != hipSuccess) {
+        skinny::g_last_hip_error = (int32_t)err;
+        return SKINNY_EHIP;
+    }
+    out->num_vgprs = attr.numRegs;
+    out->spill_bytes = (int32_t)attr.localSizeBytes;
+    out->lds_bytes_static = (int32_t)attr.sharedSizeBytes;
+    out->max_threads = attr.maxThreadsPerBlock;
+    return SKINNY_OK;
+}
+
+const char *skinny_status_string(skinny_status s) {
+    switch (s) {
+        case SKINNY_OK: return "ok";
+        case SKINNY_EINVAL: return "invalid argument (NULL pointer for a non-empty buffer, negative size or bad config field)";
+        case SKINNY_EALIGN: return "misaligned pointer (X and W need 16 bytes, R and Y 2, ACC 4)";
+        case SKINNY_ENOTSUP: return "not supported (K % 8 != 0, size limit, or configuration not built into the library)";
+        case SKINNY_EHIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+int32_t skinny_last_hip_error(void) { return skinny::g_last_hip_error; }
+
+const char *skinny_version(void) { return "0.1.0"; }
+
+}  // extern "C"

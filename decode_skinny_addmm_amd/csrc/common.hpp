@@ -1,0 +1,108 @@
+// common.hpp -- shared device helpers and the kernel registry of libskinny.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/skinny.h"
+
+namespace skinny {
+
+// ----------------------------------------------------------------------------- launch plumbing
+
+// Arguments of one call, already validated by the C ABI layer.
+struct LaunchArgs {
+    const uint16_t *X;  // bf16 [M, K]
+    const uint16_t *W;  // bf16 [N, K]
+    const uint16_t *R;  // bf16 [M, N]
+    void *out;          // bf16 [M, N] (Y) or float [M, N] (ACC)
+    int64_t M, N, K;
+    bool acc_out;       // true: write fp32 ACC instead of bf16 Y
+    hipStream_t stream;
+};
+
+// One compiled kernel instance: its public configuration, how to launch it, and the
+// address of its device function (for attribute queries).
+struct KernelEntry {
+    skinny_config cfg;
+    hipError_t (*launch)(const LaunchArgs &);
+    const void *fn_bf16;            // kernel writing bf16 Y
+    const void *fn_acc;             // kernel writing fp32 ACC
+    int64_t (*max_k)();             // largest K the instance accepts (LDS limits), or INT64_MAX
+};
+
+// Registries filled by each kernel family's translation unit.
+const KernelEntry *gemv_entries(int *count);
+const KernelEntry *mfma_entries(int *count);
+
+// ----------------------------------------------------------------------------- device helpers
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// ---- cross-lane exchange steps (gfx950) ------------------------------------------------
+// pair_step<D>(x, y): lanes whose lane-id bit D is clear return x + (x of their partner),
+// lanes with the bit set return y + (y of their partner); partners differ exactly in bit D
+// (distances 32, 16: v_permlane32_swap / v_permlane16_swap; 8: DPP row_ror:8) or pair the two
+// halves of an 8- or 4-lane group (4: DPP row_half_mirror; 2, 1: DPP quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int D>
+__device__ __forceinline__ float pair_step(float x, float y, int lane) {
+    if constexpr (D == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        constexpr int CTRL = D == 8 ? 0x128 : D == 4 ? 0x141 : D == 2 ? 0x4E : 0xB1;
+        const float xs = x + dpp_f32<CTRL>(x);
+        const float ys = y + dpp_f32<CTRL>(y);
+        return (lane & D) ? ys : xs;
+    }
+}
+
+// Transposing reduction of CNT per-lane values over the 64 lanes of a wavefront.
+// At each lane distance D (32, 16, ..., 1) a lane keeps one half of its values (the upper
+// half if its bit D is set) and adds its partner's copy of that half, so the value count
+// halves per step instead of every value paying for all six steps. After
+// s = min(log2 CNT, 6) halving steps (plain butterfly steps follow while D > 0), lane L
+// holds in a[j] the wave-wide sum of original index  j + (CNT >> s) * (L >> (6 - s));
+// lanes that differ only in their low (6 - s) bits hold the same sums.
+template <int CNT, int D, int NV>
+__device__ __forceinline__ void wave_transpose_reduce(float (&a)[NV], int lane) {
+    if constexpr (D > 0) {
+        if constexpr (CNT > 1) {
+            constexpr int H = CNT / 2;
+#pragma unroll
+            for (int i = 0; i < H; ++i) a[i] = pair_step<D>(a[i], a[i + H], lane);
+            wave_transpose_reduce<H, D / 2>(a, lane);
+        } else {
+            a[0] = pair_step<D>(a[0], a[0], lane);
+            wave_transpose_reduce<1, D / 2>(a, lane);
+        }
+    }
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+}  // namespace skinny

@@ -1,0 +1,124 @@
+"""Python binding of the skinny residual GEMM: argument marshalling over the C ABI only.
+
+Y = bf16(X @ W^T + R) for bf16 X[M,K], W[N,K], R[M,N] on the GPU; every step runs in the
+HIP kernels of libskinny.so. torch supplies device memory and the current stream.
+Argument errors raise ValueError before the library is called (as the launcher of the
+vLLM API page "fused_add_multicast_skinny_gemm" does); library errors raise SkinnyError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import CONFIG_FIELDS, SkinnyConfig, SkinnyError, SkinnyResources, check, lib  # noqa: F401
+
+
+def _as_config(cfg) -> SkinnyConfig | None:
+    if cfg is None:
+        return None
+    if isinstance(cfg, SkinnyConfig):
+        return cfg
+    if isinstance(cfg, dict):
+        vals = [int(cfg.get(f, 0)) for f in CONFIG_FIELDS]
+    else:
+        vals = [int(v) for v in cfg] + [0] * (len(CONFIG_FIELDS) - len(cfg))
+    return SkinnyConfig(*vals)
+
+
+def _check_operands(X, W, R, out, out_dtype):
+    for name, t in (("X", X), ("W", W), ("R", R), ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (row-major)" % name)
+        if t.dim() != 2:
+            raise ValueError("%s must be 2-D" % name)
+    for name, t in (("X", X), ("W", W), ("R", R)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16" % name)
+    if out.dtype != out_dtype:
+        raise ValueError("out must be %s" % out_dtype)
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K] with K = X.shape[1] (got %s vs %s)" % (tuple(W.shape), tuple(X.shape)))
+    if tuple(R.shape) != (M, N) or tuple(out.shape) != (M, N):
+        raise ValueError("R and out must be [M, N] = [%d, %d]" % (M, N))
+    devs = {t.device for t in (X, W, R, out)}
+    if len(devs) != 1:
+        raise ValueError("all operands must be on the same device")
+    return M, N, K
+
+
+def _stream_ptr(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def addmm(X: torch.Tensor, W: torch.Tensor, R: torch.Tensor, out: torch.Tensor | None = None,
+          config=None, stream=None) -> torch.Tensor:
+    """Y = bf16(X @ W^T + R) via skinny_addmm_bf16_with_config. `out` may be R (in place)."""
+    if out is None:
+        out = torch.empty_like(R)
+    M, N, K = _check_operands(X, W, R, out, torch.bfloat16)
+    c = _as_config(config)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_addmm_bf16_with_config(X.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(),
+                                                 M, N, K, ctypes.byref(c) if c is not None else None,
+                                                 _stream_ptr(stream, X.device))
+    check(st, "skinny_addmm_bf16")
+    return out
+
+
+def addmm_default(X, W, R, out, stream=None) -> torch.Tensor:
+    """The plain entry point skinny_addmm_bf16 (configuration chosen by the library)."""
+    M, N, K = _check_operands(X, W, R, out, torch.bfloat16)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_addmm_bf16(X.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(), M, N, K,
+                                     _stream_ptr(stream, X.device))
+    check(st, "skinny_addmm_bf16")
+    return out
+
+
+def addmm_acc_f32(X, W, R, out: torch.Tensor | None = None, config=None, stream=None) -> torch.Tensor:
+    """fp32 value before rounding, fp32(sum) + fp32(R), from the same kernel (test entry)."""
+    if out is None:
+        out = torch.empty(R.shape, dtype=torch.float32, device=R.device)
+    M, N, K = _check_operands(X, W, R, out, torch.float32)
+    c = _as_config(config)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_addmm_bf16_acc_f32(X.data_ptr(), W.data_ptr(), R.data_ptr(), out.data_ptr(),
+                                             M, N, K, ctypes.byref(c) if c is not None else None,
+                                             _stream_ptr(stream, X.device))
+    check(st, "skinny_addmm_bf16_acc_f32")
+    return out
+
+
+def select_config(M: int, N: int = 7168, K: int = 3584) -> dict:
+    c = SkinnyConfig()
+    check(lib().skinny_select_config(M, N, K, ctypes.byref(c)), "skinny_select_config")
+    return c.as_dict()
+
+
+def configs() -> list[dict]:
+    L = lib()
+    out = []
+    for i in range(L.skinny_num_configs()):
+        c = SkinnyConfig()
+        check(L.skinny_get_config(i, ctypes.byref(c)), "skinny_get_config")
+        out.append(c.as_dict())
+    return out
+
+
+def config_resources(config) -> dict:
+    c = _as_config(config)
+    r = SkinnyResources()
+    check(lib().skinny_config_resources(ctypes.byref(c), ctypes.byref(r)), "skinny_config_resources")
+    return {f: int(getattr(r, f)) for f, _ in SkinnyResources._fields_}
+
+
+def version() -> str:
+    return lib().skinny_version().decode()

@@ -1,0 +1,140 @@
+/*
+ * skinny.h -- C ABI of libskinny.so: the skinny residual GEMM on MI355X (gfx950).
+ *
+ * Operation (the vLLM benchmark page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py",
+ * module docstring and its torch.addmm leg; the vLLM API page
+ * "fused_add_multicast_skinny_gemm", class FusedAddMulticastSkinnyGemm, for the kernel
+ * family it comes from):
+ *
+ *     Y[m, n] = bf16( sum_{k<K} X[m, k] * W[n, k]  +  R[m, n] )
+ *
+ *   X  bf16 [M, K]  row-major, K contiguous (the activations)
+ *   W  bf16 [N, K]  row-major, K contiguous (nn.Linear weight layout; the op uses W^T)
+ *   R  bf16 [M, N]  row-major (the residual)
+ *   Y  bf16 [M, N]  row-major (the output)
+ * The products are summed in fp32, R is added in fp32, and the fp32 total is rounded once
+ * to bf16, round-to-nearest-even (alpha = beta = 1). The order of the fp32 additions is
+ * fixed per configuration, so a call is deterministic for a given configuration.
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers on the current HIP device. The caller owns every
+ *    buffer; the library allocates no device memory and never synchronises.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls are asynchronous on it and
+ *    may be captured into a HIP graph.
+ *  - Sizes: M, N, K >= 0. M == 0 or N == 0 is a no-op returning SKINNY_OK. K == 0 gives
+ *    Y = R. K must be a multiple of 8 (rows of X and W are read in 16-byte vectors).
+ *  - Alignment: X and W must be 16-byte aligned; R and Y 2-byte aligned (ACC 4-byte).
+ *    A pointer may be NULL only when its buffer is empty.
+ *  - Aliasing: Y may be exactly R (in-place residual update). Any other overlap between
+ *    an output and an input is undefined.
+ *  - Errors: argument errors are reported before anything is launched; a HIP launch error
+ *    is reported as SKINNY_EHIP (skinny_last_hip_error() gives the hipError_t value).
+ *    No C++ exception crosses this interface.
+ */
+#ifndef SKINNY_H
+#define SKINNY_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SKINNY_API __attribute__((visibility("default")))
+#else
+#define SKINNY_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum skinny_status {
+    SKINNY_OK = 0,
+    SKINNY_EINVAL = 1,  /* NULL pointer for a non-empty buffer, negative size, bad config field */
+    SKINNY_EALIGN = 2,  /* X or W not 16-byte aligned, R/Y not 2-byte aligned, ACC not 4-byte */
+    SKINNY_ENOTSUP = 3, /* K % 8 != 0, or configuration not built into this library / too large */
+    SKINNY_EHIP = 4     /* the HIP runtime reported an error when launching */
+} skinny_status;
+
+/* Kernel families. */
+enum {
+    SKINNY_PATH_GEMV = 0, /* VALU path: bf16 dot products into fp32, cross-lane reduction */
+    SKINNY_PATH_MFMA = 1  /* matrix-core path: v_mfma_f32_16x16x32_bf16 tiles */
+};
+
+/*
+ * One launch configuration (the knobs of the page-1 benchmark's Config record, re-read for
+ * 64-wide wavefronts; see each field). A configuration is usable only if the library was
+ * built with it: skinny_num_configs()/skinny_get_config() list them.
+ */
+typedef struct skinny_config {
+    int32_t path;              /* SKINNY_PATH_GEMV or SKINNY_PATH_MFMA */
+    int32_t block_size;        /* threads per workgroup, a multiple of 64 */
+    int32_t outputs_per_block; /* output columns (rows of W) per workgroup */
+    int32_t k_unroll;          /* GEMV: vectors of one W row in flight per lane per step;
+                                  MFMA: 32-wide K steps in flight per wave */
+    int32_t vector_width;      /* bf16 elements per W load per lane: 8 (16 B) or 4 (8 B) */
+    int32_t m_tile;            /* rows of X handled per pass (compile-time tile); M larger
+                                  than m_tile runs ceil(M / m_tile) passes; 0 = let the
+                                  library pick the smallest built tile >= M */
+    int32_t k_split;           /* waves of a workgroup that share the same output columns
+                                  and split K between them (their partial sums meet in LDS) */
+} skinny_config;
+
+/* Register and scratch use of one built configuration (hipFuncGetAttributes). */
+typedef struct skinny_resources {
+    int32_t num_vgprs;         /* registers per lane reported by the runtime */
+    int32_t spill_bytes;       /* private (scratch) bytes per lane; > 0 means spills */
+    int32_t lds_bytes_static;  /* static LDS per workgroup */
+    int32_t max_threads;       /* maximum threads per block for the kernel */
+} skinny_resources;
+
+/*
+ * Y = bf16(X W^T + R) with the configuration skinny_select_config() picks for (M, N, K).
+ */
+SKINNY_API skinny_status skinny_addmm_bf16(const void *X, const void *W, const void *R, void *Y,
+                                int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * The tuned configuration for a problem size (an M-indexed table measured on MI355X; the
+ * page-1 benchmark's per-M "residual_config" lookup plays the same role). Host-only, no
+ * HIP call. Returns SKINNY_EINVAL for a NULL `out` or negative sizes.
+ */
+SKINNY_API skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out);
+
+/*
+ * As skinny_addmm_bf16, with an explicit configuration (NULL = the selected one).
+ * SKINNY_ENOTSUP if that configuration is not built into the library.
+ */
+SKINNY_API skinny_status skinny_addmm_bf16_with_config(const void *X, const void *W, const void *R, void *Y,
+                                            int64_t M, int64_t N, int64_t K,
+                                            const skinny_config *cfg, void *stream);
+
+/*
+ * Test entry: the same kernel and summation order as the bf16 call, but the epilogue
+ * writes the fp32 value that would be rounded, ACC[m, n] = fp32(sum) + fp32(R[m, n]),
+ * to ACC (float [M, N], row-major). cfg NULL = the selected configuration.
+ */
+SKINNY_API skinny_status skinny_addmm_bf16_acc_f32(const void *X, const void *W, const void *R, float *ACC,
+                                        int64_t M, int64_t N, int64_t K,
+                                        const skinny_config *cfg, void *stream);
+
+/* Number of configurations built into the library, and the i-th of them (0-based). */
+SKINNY_API int32_t skinny_num_configs(void);
+SKINNY_API skinny_status skinny_get_config(int32_t index, skinny_config *out);
+
+/* Register/LDS/spill figures of a built configuration (calls hipFuncGetAttributes). */
+SKINNY_API skinny_status skinny_config_resources(const skinny_config *cfg, skinny_resources *out);
+
+/* Static text for a status code; never NULL. */
+SKINNY_API const char *skinny_status_string(skinny_status s);
+
+/* The hipError_t of the most recent SKINNY_EHIP on the calling thread (0 if none). */
+SKINNY_API int32_t skinny_last_hip_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+SKINNY_API const char *skinny_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_H */

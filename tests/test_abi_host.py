@@ -1,0 +1,132 @@
+"""Host-only checks of the C ABI library: it loads, exports every declared symbol, and its
+argument checks answer before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_skinny_addmm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("skinny.h", "skinny_probe.h")]
+
+
+def declared_functions():
+    txt = "".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"SKINNY_API\s+[\w\s\*]+?\b(skinny_\w+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libskinny.so not built")
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
+              "skinny_addmm_bf16_acc_f32", "skinny_status_string"):
+        assert f in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for f in declared_functions():
+        assert hasattr(L, f), f
+
+
+def test_only_declared_symbols_are_exported():
+    out = os.popen("nm -D --defined-only %s" % _lib.LIB_PATH).read()
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert syms == set(declared_functions())
+
+
+def test_select_config_covers_all_m(L):
+    seen = set()
+    for M in list(range(1, 300)) + [1000, 100000]:
+        c = _lib.SkinnyConfig()
+        assert L.skinny_select_config(M, 7168, 3584, ctypes.byref(c)) == 0
+        d = c.as_dict()
+        assert d["block_size"] % 64 == 0 and d["m_tile"] >= 1 and d["path"] in (0, 1)
+        seen.add(tuple(d.values()))
+    # every selected configuration is built into the library
+    built = set()
+    for i in range(L.skinny_num_configs()):
+        c = _lib.SkinnyConfig()
+        assert L.skinny_get_config(i, ctypes.byref(c)) == 0
+        built.add(tuple(c.as_dict().values()))
+    assert seen <= built
+    assert L.skinny_select_config(1, 1, 8, None) == 1
+    assert L.skinny_select_config(-1, 1, 8, ctypes.byref(_lib.SkinnyConfig())) == 1
+
+
+def test_get_config_range(L):
+    c = _lib.SkinnyConfig()
+    assert L.skinny_get_config(-1, ctypes.byref(c)) == 1
+    assert L.skinny_get_config(L.skinny_num_configs(), ctypes.byref(c)) == 1
+
+
+def test_probe_argument_checks(L):
+    assert L.skinny_probe_read(A16, -16, A16, 0, 4, None) == 1
+    assert L.skinny_probe_read(A16, 24, A16, 0, 4, None) == 2
+    assert L.skinny_probe_read(A16, 32, A16, 0, 3, None) == 1
+    assert L.skinny_probe_read(A16, 0, A16, 0, 4, None) == 0
+    assert L.skinny_probe_copy(A16, A16 + 8, 32, None) == 2
+    assert L.skinny_probe_copy(None, None, 0, None) == 0
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert len(L.skinny_status_string(s)) > 0
+    assert L.skinny_status_string(99) == b"unknown status"
+    assert L.skinny_version().decode().count(".") == 2
+
+
+# Fake device addresses: every call below must be refused by the argument checks, which
+# run before any HIP call, so nothing is dereferenced or launched.
+A16 = 0x10000
+A2 = 0x20002
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, A16, A16, -1, 8, 8), 1),          # negative M
+    ((A16, A16, A16, A16, 1, -8, 8), 1),          # negative N
+    ((A16, A16, A16, A16, 1, 8, -8), 1),          # negative K
+    ((A16, A16, A16, A16, 1, 8, 12), 3),          # K % 8 != 0
+    ((A16, A16, None, A16, 1, 8, 8), 1),          # NULL residual
+    ((A16, A16, A16, None, 1, 8, 8), 1),          # NULL output
+    ((None, A16, A16, A16, 1, 8, 8), 1),          # NULL X with K > 0
+    ((A16, None, A16, A16, 1, 8, 8), 1),          # NULL W with K > 0
+    ((A16 + 8, A16, A16, A16, 1, 8, 8), 2),       # X not 16-byte aligned
+    ((A16, A16 + 2, A16, A16, 1, 8, 8), 2),       # W not 16-byte aligned
+    ((A16, A16, A2 + 1, A16, 1, 8, 8), 2),        # R odd address
+    ((A16, A16, A16, A2 + 1, 1, 8, 8), 2),        # Y odd address
+    ((None, None, None, None, 0, 8, 8), 0),       # M == 0: no-op
+    ((None, None, None, None, 4, 0, 8), 0),       # N == 0: no-op
+])
+def test_argument_checks(L, args, expect):
+    X, W, R, Y, M, N, K = args
+    assert L.skinny_addmm_bf16(X, W, R, Y, M, N, K, None) == expect
+    assert L.skinny_addmm_bf16_with_config(X, W, R, Y, M, N, K, None, None) == expect
+    if expect != 2 or Y != A2 + 1:
+        assert L.skinny_addmm_bf16_acc_f32(X, W, R, Y, M, N, K, None, None) == expect
+
+
+def test_acc_needs_4_byte_alignment(L):
+    assert L.skinny_addmm_bf16_acc_f32(A16, A16, A16, A2, 1, 8, 8, None, None) == 2
+
+
+@pytest.mark.parametrize("cfg,expect", [
+    ((0, 100, 4, 7, 8, 1, 1), 1),     # block not a multiple of 64
+    ((0, 256, 0, 7, 8, 1, 1), 1),     # no outputs
+    ((0, 256, 4, 7, 6, 1, 1), 1),     # vector width not 4/8
+    ((0, 256, 4, 0, 8, 1, 1), 1),     # k_unroll 0
+    ((0, 256, 4, 7, 8, -1, 1), 1),    # negative m tile
+    ((0, 1024, 4, 7, 8, 1, 1), 3),    # well-formed but not built
+    ((5, 256, 4, 7, 8, 1, 1), 3),     # unknown path
+])
+def test_config_checks(L, cfg, expect):
+    c = _lib.SkinnyConfig(*cfg)
+    assert L.skinny_addmm_bf16_with_config(A16, A16, A16, A16, 1, 8, 8, ctypes.byref(c), None) == expect
