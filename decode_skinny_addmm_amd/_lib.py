@@ -5,11 +5,14 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libskinny.so")
+# SKINNY_LIB may name another build of the same C ABI (e.g. a build with different
+# compiled configurations); by default the in-tree library is used.
+LIB_PATH = os.environ.get("SKINNY_LIB") or os.path.join(PKG, "libskinny.so")
 
 STATUS = {0: "SKINNY_OK", 1: "SKINNY_EINVAL", 2: "SKINNY_EALIGN", 3: "SKINNY_ENOTSUP", 4: "SKINNY_EHIP"}
 PATH_GEMV = 0
 PATH_MFMA = 1
+PATH_MFMA_LDS = 2
 CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",

@@ -35,6 +35,7 @@ struct KernelEntry {
 // Registries filled by each kernel family's translation unit.
 const KernelEntry *gemv_entries(int *count);
 const KernelEntry *mfma_entries(int *count);
+const KernelEntry *mfma_lds_entries(int *count);
 
 // ----------------------------------------------------------------------------- device helpers
 

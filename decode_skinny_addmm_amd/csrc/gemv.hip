@@ -8,9 +8,10 @@
 //   * a workgroup is KS 64-lane waves that split K; lane l of wave w reads the 16-byte
 //     vectors (j*KS + w)*64 + l of a row, so each load instruction of a wave is one
 //     contiguous 1 KB piece of a W row (non-temporal: W is read once per call);
-//   * workgroup g owns rows g + i*G (G = number of workgroups, i = 0 .. RB*NB-1), taken in
-//     NB batches of RB rows, so the whole chip streams a compact window of W in address
-//     order; batch b+1's loads are in flight while batch b is multiplied and reduced;
+//   * workgroup g owns RB*NB rows, either g + i*G (G = number of workgroups: the chip
+//     streams a compact window of W in address order) or g*RB*NB + i (contiguous rows:
+//     outputs and residuals of a workgroup are contiguous), taken in NB batches of RB rows;
+//     batch b+1's loads are in flight while batch b is multiplied and reduced;
 //   * the lane's slice of X (KV 16-byte vectors per row of X) is loaded once into
 //     registers and reused for every row of the workgroup;
 //   * products: v_dot2c_f32_bf16 (two bf16 products into an fp32 accumulator per lane);
@@ -28,12 +29,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // MT: rows of X per pass; KS: waves (K split); RB: rows per batch; NB: batches per
 // workgroup; KV: 16-byte vectors per lane per row (K <= KV * KS * 512).
-template <int MT, int KS, int RB, int NB, int KV, bool TAIL, bool ACC>
+template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL, bool ACC>
 __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
                                                        int M, int N, int K) {
-    constexpr int V = RB * MT;                  // sums per lane per batch, index = r * MT + m
+    constexpr int V = RB * MT;                  // sums per lane per batch, index = m * RB + r
     constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
     constexpr int CF = V > 64 ? V / 64 : 1;     // sums per lane after the reduction
     constexpr int NBW = (NB + KS - 1) / KS;     // batches whose epilogue one wave runs
@@ -52,20 +53,20 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
         const int v = (j * KS + ks) * 64 + lane;
         return TAIL ? min(v, NV - 1) : v;
     };
+    // rows of this workgroup: contiguous (CONTIG) or strided over the grid
+    auto row_of = [&](int i) { return CONTIG ? g * (RB * NB) + i : g + i * G; };
     auto load_batch = [&](int b, u32x4_t (&w)[RB][KV]) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int n = min(g + (b * RB + r) * G, N - 1);  // rows past N: never stored
+            const int n = min(row_of(b * RB + r), N - 1);  // rows past N: never stored
             const u32x4_t *row = Wv + (size_t)n * NV;
 #pragma unroll
             for (int j = 0; j < KV; ++j) w[r][j] = __builtin_nontemporal_load(row + vec_index(j));
         }
     };
 
-    // 1. the first two batches of W, then this lane's slice of X, then residuals
-    u32x4_t wbuf[2][RB][KV];
-    load_batch(0, wbuf[0]);
-    if constexpr (NB > 1) load_batch(1, wbuf[1]);
+    // 1. this lane's slice of X, then the first two batches of W, then residuals (the wait
+    // counter retires loads in issue order, so X and batch 0 must not sit behind batch 1)
     u32x4_t x[KV][MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -73,6 +74,12 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < KV; ++j) x[j][m] = row[vec_index(j)];
     }
+    u32x4_t wbuf[2][RB][KV];
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: X, batch 0, batch 1
+    load_batch(0, wbuf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NB > 1) load_batch(1, wbuf[1]);
+    __builtin_amdgcn_sched_barrier(0);
     const bool writer_lane = (lane & ((64 >> S) - 1)) == 0;
     const int base = CF * (lane >> (6 - S));
     float rres[NBW][CF];
@@ -82,8 +89,8 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
 #pragma unroll
         for (int c = 0; c < CF; ++c) {
             const int idx = base + c;
-            const int n = min(g + (b * RB + idx / MT) * G, N - 1);
-            const int m = min(m0 + idx % MT, M - 1);
+            const int n = min(row_of(b * RB + idx % RB), N - 1);
+            const int m = min(m0 + idx / RB, M - 1);
             rres[q][c] = bf16_bits_to_f32(R[(size_t)m * N + n]);
         }
     }
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
                     for (int d = 0; d < 4; ++d)
-                        acc[r * MT + m] = dot2_bf16(x[j][m][d], w[r][j][d], acc[r * MT + m]);
+                        acc[m * RB + r] = dot2_bf16(x[j][m][d], w[r][j][d], acc[m * RB + r]);
         if (b + 2 < NB) load_batch(b + 2, w);  // refill this buffer while the next batch lands
         wave_transpose_reduce<V, 32>(acc, lane);
         if (writer_lane) {
@@ -137,8 +144,8 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
 #pragma unroll
         for (int c = 0; c < CF; ++c) {
             const int idx = base + c;
-            const int n = g + (b * RB + idx / MT) * G;
-            const int m = m0 + idx % MT;
+            const int n = row_of(b * RB + idx % RB);
+            const int m = m0 + idx / RB;
             if (m < M && n < N) {
                 float t = red[b][0][idx];
 #pragma unroll
@@ -154,25 +161,25 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
     }
 }
 
-template <int MT, int KS, int RB, int NB, int KV, bool TAIL>
+template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL>
 void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
     if (a.acc_out)
-        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, TAIL, true>), grid, block, 0, a.stream, a.X, a.W,
-                           a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, true>), grid, block, 0, a.stream, a.X,
+                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
     else
-        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, TAIL, false>), grid, block, 0, a.stream, a.X, a.W,
-                           a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, false>), grid, block, 0, a.stream, a.X,
+                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
 }
 
-template <int MT, int KS, int RB, int NB, int KV>
+template <int MT, int KS, int RB, int NB, int KV, bool CONTIG>
 hipError_t launch_gemv(const LaunchArgs &a) {
     constexpr int64_t rows = (int64_t)RB * NB;
     dim3 grid((unsigned)((a.N + rows - 1) / rows), (unsigned)((a.M + MT - 1) / MT));
     dim3 block(KS * 64);
     if (a.K % ((int64_t)KV * KS * 512) == 0)
-        launch_one<MT, KS, RB, NB, KV, false>(a, grid, block);
+        launch_one<MT, KS, RB, NB, KV, CONTIG, false>(a, grid, block);
     else
-        launch_one<MT, KS, RB, NB, KV, true>(a, grid, block);
+        launch_one<MT, KS, RB, NB, KV, CONTIG, true>(a, grid, block);
     return hipGetLastError();
 }
 
@@ -180,13 +187,14 @@ template <int KS, int KV>
 int64_t gemv_max_k() { return (int64_t)KV * KS * 64 * 8; }
 
 // Public knobs: block_size = 64*KS, outputs_per_block = RB*NB, k_unroll = KV,
-// vector_width = 8, m_tile = MT, k_split = KS; rows per batch RB = outputs_per_block / NB.
-#define GEMV_ENTRY(MT, KS, RB, NB, KV)                                                             \
+// vector_width = 8 (rows strided over the grid) or 9 (contiguous rows), m_tile = MT,
+// k_split = KS; rows per batch RB = outputs_per_block / NB.
+#define GEMV_ENTRY(MT, KS, RB, NB, KV, CONTIG)                                                     \
     KernelEntry {                                                                                  \
-        skinny_config{SKINNY_PATH_GEMV, 64 * KS, RB * NB, KV, 8, MT, KS},                          \
-            &launch_gemv<MT, KS, RB, NB, KV>,                                                      \
-            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, false, false>,                          \
-            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, false, true>, &gemv_max_k<KS, KV>       \
+        skinny_config{SKINNY_PATH_GEMV, 64 * KS, RB * NB, KV, CONTIG ? 9 : 8, MT, KS},             \
+            &launch_gemv<MT, KS, RB, NB, KV, CONTIG>,                                              \
+            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, false>,                  \
+            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, true>, &gemv_max_k<KS, KV> \
     }
 
 #include "gemv_instances.inc"

@@ -54,8 +54,10 @@ def test_small_shapes_every_config(sk):
         Yo, Ao = full_oracle(X, ws[0], rs[0])
         for cfg in all_configs(sk):
             print("small shape", (M, N, K), "config", cfg, flush=True)
-            if cfg["path"] == 0 and K > cfg["k_unroll"] * cfg["k_split"] * 512:
-                # GEMV instances hold their K slice in registers: larger K is refused
+            too_long = ((cfg["path"] == 0 and K > cfg["k_unroll"] * cfg["k_split"] * 512) or
+                        (cfg["path"] == 2 and K > cfg["k_split"] * 512))
+            if too_long:
+                # GEMV and LDS-MFMA instances hold their K slice on chip: larger K is refused
                 with pytest.raises(sk.ops.SkinnyError) as ei:
                     run_both(sk, X, ws[0], rs[0], cfg)
                 assert ei.value.status == 3
