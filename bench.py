@@ -43,6 +43,32 @@ def algorithmic_bytes(M: int, N: int = N_DIM, K: int = K_DIM) -> int:
     return 2 * N * K + 2 * M * K + 2 * M * N + 2 * M * N
 
 
+def lookup_traffic(cfg: dict, M: int):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE/WRITE_SIZE runs for this exact
+    kernel configuration and M (profiles/traffic.json, scaled by a copy-kernel calibration);
+    None when absent or when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        entries = json.load(open(path))["entries"]
+    except (OSError, ValueError, KeyError):
+        return None
+    for e in entries:
+        if e.get("config") != cfg or e.get("M") != M or e.get("N") != N_DIM or e.get("K") != K_DIM:
+            continue
+        h = hashlib.sha256()
+        try:
+            for f in e["source_files"]:
+                h.update(open(os.path.join(ROOT, "decode_skinny_addmm_amd", "csrc", f), "rb").read())
+        except OSError:
+            return None
+        if h.hexdigest() != e.get("source_sha256"):
+            return None
+        return {"bytes": e["traffic_bytes"], "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+                "source": "profiles/" + e["summary"]}
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -280,6 +306,22 @@ def run_probe(args, sk):
         out.close()
 
 
+def run_calib(args, sk):
+    """Plain copy of a known size (the read+write reference for byte counters)."""
+    import torch
+    L = sk.ops.lib()
+    nbytes = N_DIM * K_DIM * 2
+    src = torch.randn(nbytes // 2, dtype=torch.float32, device="cuda").view(torch.bfloat16)[: nbytes // 2]
+    src = src.contiguous()
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.steps)):
+        sk.ops.check(L.skinny_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes,
+                                         torch.cuda.current_stream().cuda_stream), "probe_copy")
+    torch.cuda.synchronize()
+    print(json.dumps({"calib": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": max(1, args.steps)}), flush=True)
+
+
 def make_launch(sk, config):
     if config is None:
         return lambda X, W, R, Y: sk.addmm_default(X, W, R, Y)
@@ -325,7 +367,9 @@ def run_default(args, sk):
         "us_per_call": round(mean_us, 4),
         "us_per_call_stats": {k: round(v, 4) for k, v in st.items()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (lambda t: t["bytes"] if t else None)(lookup_traffic(cfg, M)),
+                     "traffic_detail": lookup_traffic(cfg, M),
                      "bytes_per_launch": algorithmic_bytes(M),
                      "mfma_frac": round(flops / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "device": torch.cuda.get_device_name(0),
@@ -381,7 +425,7 @@ def main():
     p.add_argument("--copies", type=int, default=6)
     p.add_argument("--calls", type=int, default=500, help="launches captured per graph (one step)")
     p.add_argument("--config", type=parse_config, default=None)
-    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe"), default="default")
+    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib"), default="default")
     p.add_argument("--out", type=str, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -403,6 +447,8 @@ def main():
         run_default(args, sk)
     elif args.mode == "probe":
         run_probe(args, sk)
+    elif args.mode == "calib":
+        run_calib(args, sk)
     elif args.mode == "sweep":
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
         sweep_rows(args, sk, Ms, lambda m: [c for c in sk.configs()])
