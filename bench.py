@@ -431,6 +431,7 @@ def main():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")
     p.add_argument("--ms", type=str, default=None, help="comma-separated M list for sweep/mcurve")
+    p.add_argument("--paths", type=str, default=None, help="sweep only these kernel paths (comma-separated ids)")
     args = p.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -451,7 +452,11 @@ def main():
         run_calib(args, sk)
     elif args.mode == "sweep":
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
-        sweep_rows(args, sk, Ms, lambda m: [c for c in sk.configs()])
+        paths = {int(x) for x in args.paths.split(",")} if args.paths else None
+        # configurations that would re-read W more than 4 times (ceil(M / m_tile) passes) are
+        # skipped: they are never competitive and take long to time
+        sweep_rows(args, sk, Ms, lambda m: [c for c in sk.configs()
+                                            if -(-m // c["m_tile"]) <= 4 and (paths is None or c["path"] in paths)])
     else:
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else (
             [args.m] if args.m else [1, 2, 4, 8, 16, 32, 64, 128, 256])

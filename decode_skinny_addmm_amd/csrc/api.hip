@@ -24,6 +24,8 @@ struct Registry {
         for (int i = 0; i < n; ++i) all.push_back(&f[i]);
         const KernelEntry *l = mfma_lds_entries(&n);
         for (int i = 0; i < n; ++i) all.push_back(&l[i]);
+        const KernelEntry *t = gemm_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&t[i]);
     }
 };
 
@@ -98,7 +100,8 @@ skinny_status run(const void *X, const void *W, const void *R, void *out, bool a
     if (K > e->max_k()) return SKINNY_ENOTSUP;
     // K == 0 (Y = R): the GEMV and LDS-MFMA kernels load their K slice unconditionally, so the empty
     // sum goes to the general kernel, whose K loop simply does not run.
-    if (K == 0 && e->cfg.path != SKINNY_PATH_MFMA) e = find_entry(kFallbackSmall, M);
+    if (K == 0 && (e->cfg.path == SKINNY_PATH_GEMV || e->cfg.path == SKINNY_PATH_MFMA_LDS))
+        e = find_entry(kFallbackSmall, M);
     if (!e) return SKINNY_ENOTSUP;
     const int64_t mt = e->cfg.m_tile;
     if ((M + mt - 1) / mt > 65535) return SKINNY_ENOTSUP;

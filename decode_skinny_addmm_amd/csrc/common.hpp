@@ -36,6 +36,7 @@ struct KernelEntry {
 const KernelEntry *gemv_entries(int *count);
 const KernelEntry *mfma_entries(int *count);
 const KernelEntry *mfma_lds_entries(int *count);
+const KernelEntry *gemm_entries(int *count);
 
 // ----------------------------------------------------------------------------- device helpers
 

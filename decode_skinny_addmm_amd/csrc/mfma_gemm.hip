@@ -1,0 +1,220 @@
+// mfma_gemm.hip -- LDS-tiled matrix-core path for larger M (tens to hundreds of rows of X).
+//
+// Operation: vLLM benchmark page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py"
+// (module docstring; torch.addmm leg): Y = bf16(X W^T + R), fp32 accumulation. When M is in
+// the tens or hundreds, every workgroup can no longer hold all of X on chip, so this kernel
+// is a classic K-loop GEMM shaped for gfx950:
+//   * a workgroup computes a BN x BM block of Y^T (BN rows of W = output columns n, BM rows
+//     of X) with 4 waves in a 2 x 2 layout, each wave a (BN/2) x (BM/2) block of
+//     v_mfma_f32_16x16x32_bf16 tiles;
+//   * K advances in stages of 128: both operand tiles are fetched with 16-byte loads (W
+//     non-temporal), D stages ahead into registers so HBM latency is covered, then written
+//     to LDS (rows padded to 272 bytes: fragment reads hit distinct banks) and read back as
+//     A (W) and B (X^T) fragments;
+//   * block ids are laid out so that the M-tiles of one W row tile are consecutive on the
+//     same XCD (blocks are dealt to the 8 XCDs round-robin): they run together and share
+//     the W tile through that XCD's L2, so W leaves HBM once;
+//   * the epilogue stages the fp32 block in LDS and walks it row by row of Y, so residual
+//     loads and output stores are contiguous; R is added in fp32, one RNE rounding to bf16.
+#include "common.hpp"
+
+namespace skinny {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKC = 128;                 // K per stage (bf16 elements)
+constexpr int kPitch = kKC * 2 + 16;     // bytes per staged row (256 + 16 padding)
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// BN: rows of W per workgroup; BM: rows of X per workgroup; D: stages in flight.
+template <int BN, int BM, int D, bool ACC>
+__global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restrict__ X,
+                                                        const uint16_t *__restrict__ W,
+                                                        const uint16_t *R, void *out,
+                                                        int M, int N, int K, int n_tiles, int m_tiles) {
+    constexpr int WN = BN / 2, WM = BM / 2;          // wave block
+    constexpr int TN = WN / 16, TM = WM / 16;        // MFMA tiles per wave
+    constexpr int LW = BN * 16 / 256;                // 16-byte W loads per thread per stage
+    constexpr int LX = BM * 16 / 256;                // 16-byte X loads per thread per stage
+    static_assert(LW >= 1 && LX >= 1 && TN >= 1 && TM >= 1, "tile too small");
+    constexpr int STAGE_BYTES = (BN + BM) * kPitch;
+    constexpr int CBYTES = BN * (BM + 4) * 4;        // fp32 block for the epilogue (padded)
+    constexpr int LDS_BYTES = STAGE_BYTES > CBYTES ? STAGE_BYTES : CBYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+    uint8_t *Ws = lds;
+    uint8_t *Xs = lds + BN * kPitch;
+
+    // XCD-aware block order: block b runs on XCD b % 8; consecutive blocks of one XCD take
+    // the m-tiles of one n-tile
+    const int b = blockIdx.x;
+    const int xcd = b & 7, j = b >> 3;
+    const int mt = j % m_tiles;
+    const int nt = (j / m_tiles) * 8 + xcd;
+    if (nt >= n_tiles) return;                       // padding block (uniform)
+    const int n0 = nt * BN, m0 = mt * BM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = (wave & 1) * WN, wm = (wave >> 1) * WM;
+    const int KV = K >> 3;                           // 16-byte vectors per row
+    const int stages = (K + kKC - 1) / kKC;
+    const u32x4_t *Wv = reinterpret_cast<const u32x4_t *>(W);
+    const u32x4_t *Xv = reinterpret_cast<const u32x4_t *>(X);
+
+    // thread -> (row, 16-byte column) of the stage tiles: 16 threads cover one 256-byte row
+    const int lrow = tid >> 4, lcol = tid & 15;
+    auto fetch = [&](int s, u32x4_t (&wr)[LW], u32x4_t (&xr)[LX]) {
+        const int v = min(s * (kKC / 8) + lcol, KV - 1);   // clamped; zeroed below if past K
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const int n = min(n0 + lrow + 16 * i, N - 1);
+            wr[i] = __builtin_nontemporal_load(Wv + (size_t)n * KV + v);
+        }
+#pragma unroll
+        for (int i = 0; i < LX; ++i) {
+            const int m = min(m0 + lrow + 16 * i, M - 1);
+            xr[i] = Xv[(size_t)m * KV + v];
+        }
+    };
+    auto stash = [&](int s, u32x4_t (&wr)[LW], u32x4_t (&xr)[LX]) {
+        const bool kok = s * (kKC / 8) + lcol < KV;
+#pragma unroll
+        for (int i = 0; i < LW; ++i)
+            *reinterpret_cast<u32x4_t *>(Ws + (lrow + 16 * i) * kPitch + 16 * lcol) = kok ? wr[i] : u32x4_t{};
+#pragma unroll
+        for (int i = 0; i < LX; ++i)
+            *reinterpret_cast<u32x4_t *>(Xs + (lrow + 16 * i) * kPitch + 16 * lcol) = kok ? xr[i] : u32x4_t{};
+    };
+
+    f32x4_t acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int c = 0; c < TM; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wr[D][LW], xr[D][LX];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < stages) fetch(d, wr[d], xr[d]);
+
+    const int frow = lane & 15, fk = 16 * (lane >> 4);  // fragment row / byte offset in a k-step
+    for (int s0 = 0; s0 < stages; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int s = s0 + d;
+            if (s < stages) {                        // uniform
+                __syncthreads();                     // previous stage's fragment reads are done
+                stash(s, wr[d], xr[d]);
+                __syncthreads();
+                if (s + D < stages) fetch(s + D, wr[d], xr[d]);
+                // each stage sums into a fresh tile that is then added to the total: the
+                // longest fp32 rounding chain is 4 + K/128 steps instead of K/32
+                f32x4_t st[TN][TM];
+#pragma unroll
+                for (int a = 0; a < TN; ++a)
+#pragma unroll
+                    for (int c = 0; c < TM; ++c) st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < kKC / 32; ++kk) {
+                    u32x4_t af[TN], bfr[TM];
+#pragma unroll
+                    for (int a = 0; a < TN; ++a)
+                        af[a] = *reinterpret_cast<const u32x4_t *>(Ws + (wn + 16 * a + frow) * kPitch + 64 * kk + fk);
+#pragma unroll
+                    for (int c = 0; c < TM; ++c)
+                        bfr[c] = *reinterpret_cast<const u32x4_t *>(Xs + (wm + 16 * c + frow) * kPitch + 64 * kk + fk);
+#pragma unroll
+                    for (int a = 0; a < TN; ++a)
+#pragma unroll
+                        for (int c = 0; c < TM; ++c) st[a][c] = mfma16(af[a], bfr[c], st[a][c]);
+                }
+#pragma unroll
+                for (int a = 0; a < TN; ++a)
+#pragma unroll
+                    for (int c = 0; c < TM; ++c) acc[a][c] += st[a][c];
+            }
+        }
+    }
+
+    // epilogue: acc[a][c][r] = Y^T[n0 + wn + 16a + 4*(lane/16) + r][m0 + wm + 16c + lane%16]
+    __syncthreads();
+    float *C = reinterpret_cast<float *>(lds);       // C[n][m], row pitch BM + 4 floats
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int c = 0; c < TM; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                C[(wn + 16 * a + 4 * (lane >> 4) + r) * (BM + 4) + wm + 16 * c + (lane & 15)] = acc[a][c][r];
+    __syncthreads();
+    // walk the block row by row of Y: neighbouring threads take neighbouring n
+#pragma unroll 4
+    for (int e = tid; e < BN * BM; e += 256) {
+        const int ml = e / BN, nl = e % BN;
+        const int m = m0 + ml, n = n0 + nl;
+        if (m < M && n < N) {
+            const size_t o = (size_t)m * N + n;
+            const float y = C[nl * (BM + 4) + ml] + bf16_bits_to_f32(R[o]);
+            if constexpr (ACC)
+                static_cast<float *>(out)[o] = y;
+            else
+                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+        }
+    }
+}
+
+template <int BN, int BM, int D>
+hipError_t launch_gemm(const LaunchArgs &a) {
+    const int n_tiles = (int)((a.N + BN - 1) / BN);
+    const int m_tiles = (int)((a.M + BM - 1) / BM);
+    const int groups = (n_tiles + 7) / 8;            // n-tiles per XCD, rounded up
+    dim3 grid((unsigned)(groups * 8 * m_tiles));
+    dim3 block(256);
+    if (a.acc_out)
+        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+    else
+        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+    return hipGetLastError();
+}
+
+int64_t gemm_max_k() { return INT64_MAX; }
+
+// Public knobs: path SKINNY_PATH_GEMM, block_size 256, outputs_per_block = BN,
+// k_unroll = D (stages in flight), vector_width = 8, m_tile = BM, k_split = 1.
+#define GEMM_ENTRY(BN, BM, D)                                                                      \
+    KernelEntry {                                                                                  \
+        skinny_config{SKINNY_PATH_GEMM, 256, BN, D, 8, BM, 1}, &launch_gemm<BN, BM, D>,            \
+            (const void *)&mfma_gemm_kernel<BN, BM, D, false>,                                     \
+            (const void *)&mfma_gemm_kernel<BN, BM, D, true>, &gemm_max_k                          \
+    }
+
+const KernelEntry kGemmEntries[] = {
+    GEMM_ENTRY(32, 32, 4),
+    GEMM_ENTRY(32, 64, 3),
+    GEMM_ENTRY(32, 64, 4),
+    GEMM_ENTRY(64, 64, 3),
+    GEMM_ENTRY(32, 128, 3),
+    GEMM_ENTRY(64, 128, 2),
+    GEMM_ENTRY(64, 128, 3),
+    GEMM_ENTRY(32, 256, 2),
+    GEMM_ENTRY(64, 256, 2),
+};
+
+}  // namespace
+
+const KernelEntry *gemm_entries(int *count) {
+    *count = (int)(sizeof(kGemmEntries) / sizeof(kGemmEntries[0]));
+    return kGemmEntries;
+}
+
+}  // namespace skinny

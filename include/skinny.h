@@ -58,8 +58,10 @@ typedef enum skinny_status {
 enum {
     SKINNY_PATH_GEMV = 0, /* VALU path: bf16 dot products into fp32, cross-lane reduction */
     SKINNY_PATH_MFMA = 1, /* matrix-core path, fragments loaded straight from memory; any K */
-    SKINNY_PATH_MFMA_LDS = 2 /* matrix-core path, W streamed in 1 KB row pieces and turned
-                                into fragments through LDS; K <= 512 * k_split */
+    SKINNY_PATH_MFMA_LDS = 2, /* matrix-core path, W streamed in 1 KB row pieces and turned
+                                 into fragments through LDS; K <= 512 * k_split */
+    SKINNY_PATH_GEMM = 3      /* matrix-core K-loop GEMM with LDS-staged operand tiles, for
+                                 larger M; any K */
 };
 
 /*
@@ -68,7 +70,7 @@ enum {
  * built with it: skinny_num_configs()/skinny_get_config() list them.
  */
 typedef struct skinny_config {
-    int32_t path;              /* SKINNY_PATH_GEMV, SKINNY_PATH_MFMA or SKINNY_PATH_MFMA_LDS */
+    int32_t path;              /* one of the SKINNY_PATH_* values */
     int32_t block_size;        /* threads per workgroup, a multiple of 64 */
     int32_t outputs_per_block; /* output columns (rows of W) per workgroup */
     int32_t k_unroll;          /* GEMV: vectors of one W row in flight per lane per step;
