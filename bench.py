@@ -323,6 +323,9 @@ def run_calib(args, sk):
 
 
 def make_launch(sk, config):
+    if config is not None and config.get("reference") == "torch.addmm":
+        import torch
+        return lambda X, W, R, Y: torch.addmm(R, X, W.t(), out=Y)
     if config is None:
         return lambda X, W, R, Y: sk.addmm_default(X, W, R, Y)
     return lambda X, W, R, Y: sk.addmm(X, W, R, out=Y, config=config)
@@ -401,6 +404,7 @@ def sweep_rows(args, sk, Ms, config_lists):
                 launch, samples, mean_us, gbs = measure(sk, wl, cfg, args.calls, args.warmup, args.steps)
                 row.update(summarize(samples))
                 row.update({"mean_us_total": mean_us, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                            "mfma_frac": 2.0 * M * N_DIM * K_DIM / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                             "resources": sk.config_resources(cfg) if cfg.get("m_tile") else None,
                             "max_ulp_sampled": oracle_parity_sample(wl, launch, 256)})
             except Exception as e:  # noqa: BLE001
@@ -432,6 +436,8 @@ def main():
     p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")
     p.add_argument("--ms", type=str, default=None, help="comma-separated M list for sweep/mcurve")
     p.add_argument("--paths", type=str, default=None, help="sweep only these kernel paths (comma-separated ids)")
+    p.add_argument("--with-torch", action="store_true",
+                   help="mcurve: add torch.addmm (the vendor library) as a context row")
     args = p.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -460,7 +466,8 @@ def main():
     else:
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else (
             [args.m] if args.m else [1, 2, 4, 8, 16, 32, 64, 128, 256])
-        sweep_rows(args, sk, Ms, lambda m: [args.config or sk.select_config(m)])
+        sweep_rows(args, sk, Ms, lambda m: [args.config or sk.select_config(m)] +
+                   ([{"reference": "torch.addmm"}] if args.with_torch else []))
 
 
 if __name__ == "__main__":

@@ -92,15 +92,15 @@ skinny_status run(const void *X, const void *W, const void *R, void *out, bool a
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return SKINNY_ENOTSUP;
     const skinny_config c = cfg ? *cfg : select(M, K);
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
-        c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 11 || c.m_tile < 0 ||
+        c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
         c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0)
         return SKINNY_EINVAL;
     const KernelEntry *e = find_entry(c, M);
     if (!e) return SKINNY_ENOTSUP;
     if (K > e->max_k()) return SKINNY_ENOTSUP;
-    // K == 0 (Y = R): the GEMV and LDS-MFMA kernels load their K slice unconditionally, so the empty
+    // K == 0 (Y = R): all kernels but the direct MFMA one issue their first loads unconditionally, so the empty
     // sum goes to the general kernel, whose K loop simply does not run.
-    if (K == 0 && (e->cfg.path == SKINNY_PATH_GEMV || e->cfg.path == SKINNY_PATH_MFMA_LDS))
+    if (K == 0 && e->cfg.path != SKINNY_PATH_MFMA)
         e = find_entry(kFallbackSmall, M);
     if (!e) return SKINNY_ENOTSUP;
     const int64_t mt = e->cfg.m_tile;

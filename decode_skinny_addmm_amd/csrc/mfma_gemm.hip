@@ -7,8 +7,8 @@
 //   * a workgroup computes a BN x BM block of Y^T (BN rows of W = output columns n, BM rows
 //     of X) with 4 waves in a 2 x 2 layout, each wave a (BN/2) x (BM/2) block of
 //     v_mfma_f32_16x16x32_bf16 tiles;
-//   * K advances in stages of 128: both operand tiles are fetched with 16-byte loads (W
-//     non-temporal), D stages ahead into registers so HBM latency is covered, then written
+//   * K advances in stages of 128: both operand tiles are fetched with 16-byte loads, D
+//     stages ahead into registers so HBM latency is covered, then written
 //     to LDS (rows padded to 272 bytes: fragment reads hit distinct banks) and read back as
 //     A (W) and B (X^T) fragments;
 //   * block ids are laid out so that the M-tiles of one W row tile are consecutive on the
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
             const int n = min(n0 + lrow + 16 * i, N - 1);
-            wr[i] = __builtin_nontemporal_load(Wv + (size_t)n * KV + v);
+            wr[i] = Wv[(size_t)n * KV + v];  // cached: the other m-tiles read it from L2
         }
 #pragma unroll
         for (int i = 0; i < LX; ++i) {
@@ -100,47 +100,48 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
 #pragma unroll
         for (int c = 0; c < TM; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // The loop body is branch-free so the compiler keeps D stages of loads in flight (a
+    // branch around a load makes it wait for every outstanding load): prefetches past the
+    // last stage re-read the last stage (never used), stages past K are zero-filled.
     u32x4_t wr[D][LW], xr[D][LX];
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < stages) fetch(d, wr[d], xr[d]);
+    for (int d = 0; d < D; ++d) fetch(min(d, stages - 1), wr[d], xr[d]);
 
     const int frow = lane & 15, fk = 16 * (lane >> 4);  // fragment row / byte offset in a k-step
-    for (int s0 = 0; s0 < stages; s0 += D) {
+    const int groups = (stages + D - 1) / D;
+    for (int g0 = 0; g0 < groups; ++g0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int s = s0 + d;
-            if (s < stages) {                        // uniform
-                __syncthreads();                     // previous stage's fragment reads are done
-                stash(s, wr[d], xr[d]);
-                __syncthreads();
-                if (s + D < stages) fetch(s + D, wr[d], xr[d]);
-                // each stage sums into a fresh tile that is then added to the total: the
-                // longest fp32 rounding chain is 4 + K/128 steps instead of K/32
-                f32x4_t st[TN][TM];
+            const int s = g0 * D + d;
+            __syncthreads();                         // previous stage's fragment reads are done
+            stash(s, wr[d], xr[d]);
+            __syncthreads();
+            fetch(min(s + D, stages - 1), wr[d], xr[d]);
+            // each stage sums into a fresh tile that is then added to the total: the longest
+            // fp32 rounding chain is 4 + K/128 steps instead of K/32
+            f32x4_t st[TN][TM];
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int c = 0; c < TM; ++c) st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < kKC / 32; ++kk) {
+                u32x4_t af[TN], bfr[TM];
+#pragma unroll
+                for (int a = 0; a < TN; ++a)
+                    af[a] = *reinterpret_cast<const u32x4_t *>(Ws + (wn + 16 * a + frow) * kPitch + 64 * kk + fk);
+#pragma unroll
+                for (int c = 0; c < TM; ++c)
+                    bfr[c] = *reinterpret_cast<const u32x4_t *>(Xs + (wm + 16 * c + frow) * kPitch + 64 * kk + fk);
 #pragma unroll
                 for (int a = 0; a < TN; ++a)
 #pragma unroll
-                    for (int c = 0; c < TM; ++c) st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < kKC / 32; ++kk) {
-                    u32x4_t af[TN], bfr[TM];
-#pragma unroll
-                    for (int a = 0; a < TN; ++a)
-                        af[a] = *reinterpret_cast<const u32x4_t *>(Ws + (wn + 16 * a + frow) * kPitch + 64 * kk + fk);
-#pragma unroll
-                    for (int c = 0; c < TM; ++c)
-                        bfr[c] = *reinterpret_cast<const u32x4_t *>(Xs + (wm + 16 * c + frow) * kPitch + 64 * kk + fk);
-#pragma unroll
-                    for (int a = 0; a < TN; ++a)
-#pragma unroll
-                        for (int c = 0; c < TM; ++c) st[a][c] = mfma16(af[a], bfr[c], st[a][c]);
-                }
-#pragma unroll
-                for (int a = 0; a < TN; ++a)
-#pragma unroll
-                    for (int c = 0; c < TM; ++c) acc[a][c] += st[a][c];
+                    for (int c = 0; c < TM; ++c) st[a][c] = mfma16(af[a], bfr[c], st[a][c]);
             }
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int c = 0; c < TM; ++c) acc[a][c] += st[a][c];
         }
     }
 
@@ -200,14 +201,15 @@ int64_t gemm_max_k() { return INT64_MAX; }
 
 const KernelEntry kGemmEntries[] = {
     GEMM_ENTRY(32, 32, 4),
-    GEMM_ENTRY(32, 64, 3),
+    GEMM_ENTRY(32, 32, 7),
     GEMM_ENTRY(32, 64, 4),
-    GEMM_ENTRY(64, 64, 3),
-    GEMM_ENTRY(32, 128, 3),
+    GEMM_ENTRY(32, 64, 2),
+    GEMM_ENTRY(64, 64, 2),
+    GEMM_ENTRY(64, 64, 4),
+    GEMM_ENTRY(32, 128, 2),
+    GEMM_ENTRY(32, 128, 4),
     GEMM_ENTRY(64, 128, 2),
-    GEMM_ENTRY(64, 128, 3),
     GEMM_ENTRY(32, 256, 2),
-    GEMM_ENTRY(64, 256, 2),
 };
 
 }  // namespace

@@ -34,8 +34,9 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 // CONTIG: workgroup g owns the contiguous rows g*RB*NB + i instead of g + i*G.
-// XL: X fragments are built from contiguous 1 KB row loads (only the rows < M) passed
-// through the staging slice, instead of loaded in fragment order (16 rows x 64 B each).
+// XL: the rows of X (those < M) are loaded first, in contiguous 1 KB pieces, and turned into
+// fragments through the staging slice; otherwise the fragments are loaded in fragment order
+// (16 rows x 64 B per instruction) after the W batches.
 template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL, bool ACC>
 __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__restrict__ X,
                                                            const uint16_t *__restrict__ W,
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
     const u32x4_t *Wv = reinterpret_cast<const u32x4_t *>(W);
     const u32x4_t *Xv = reinterpret_cast<const u32x4_t *>(X);
 
-    constexpr int SROWS = (XL && RB < 16) ? 16 : RB;  // staged rows per wave
+    constexpr int SROWS = (XL && RB < 16) ? 16 : RB;  // staged rows per wave (X needs 16)
     __shared__ __attribute__((aligned(16))) uint8_t stage[KS][SROWS * kRowPitch];
     __shared__ f32x4_t red[NB][KS][CT][LV];
 
@@ -72,8 +73,15 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
         }
     };
 
-    // W batches 0 and 1 are asked for first, then X
     u32x4_t wbuf[2][RB];
+    u32x4_t xrow[XL ? 16 * CT : 1];
+    if constexpr (XL && !TAIL) {
+        // X first (only the rows < M; the first four of each column tile unconditionally):
+        // waiting for X then does not wait for W, whose loads follow
+#pragma unroll
+        for (int i = 0; i < 16 * CT; ++i)
+            if ((i & 15) < 4 || m0 + i < M) xrow[i] = Xv[(size_t)min(m0 + i, M - 1) * NV + vlane];
+    }
     load_batch(0, wbuf[0]);
     if constexpr (NB > 1) load_batch(1, wbuf[1]);
 
@@ -81,18 +89,16 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
     uint8_t *my = stage[ks];
     u32x4_t xf[16][CT];
     if constexpr (XL && !TAIL) {
-        // rows of X (those < M) in 1 KB pieces through the staging slice, 16 rows at a time
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + 16 * c + i;
-                if (m < M)  // uniform: same for every lane
-                    *reinterpret_cast<u32x4_t *>(my + i * kRowPitch + 16 * lane) = Xv[(size_t)m * NV + vlane];
-            }
+            for (int i = 0; i < 16; ++i)
+                if (i < 4 || m0 + 16 * c + i < M)
+                    *reinterpret_cast<u32x4_t *>(my + i * kRowPitch + 16 * lane) = xrow[16 * c + i];
+            const int valid = max(min(M - m0 - 16 * c, 16), 1);  // rows of this column tile < M
 #pragma unroll
             for (int s = 0; s < 16; ++s)
-                xf[s][c] = *reinterpret_cast<const u32x4_t *>(my + min(lane & 15, max(M - m0 - 16 * c, 1) - 1) * kRowPitch +
+                xf[s][c] = *reinterpret_cast<const u32x4_t *>(my + min(lane & 15, valid - 1) * kRowPitch +
                                                               64 * s + 16 * (lane >> 4));
         }
     } else {
@@ -195,6 +201,7 @@ void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
 
 template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL>
 hipError_t launch_mfma_lds(const LaunchArgs &a) {
+    static_assert(!XL || CONTIG, "X-first variants use contiguous rows");
     constexpr int64_t rows = (int64_t)RB * NB;
     dim3 grid((unsigned)((a.N + rows - 1) / rows), (unsigned)((a.M + 16 * CT - 1) / (16 * CT)));
     dim3 block(KS * 64);
@@ -209,12 +216,12 @@ template <int KS>
 int64_t lds_max_k() { return (int64_t)KS * 512; }
 
 // Public knobs: path SKINNY_PATH_MFMA_LDS, block_size = 64*KS, outputs_per_block = RB*NB,
-// k_unroll = RB (rows per batch), vector_width = 8, m_tile = 16*CT, k_split = KS.
-// Variants of one shape are told apart by vector_width: 8 = strided rows, X in fragment
-// order; 9 = contiguous rows; 10 = strided rows, X through LDS; 11 = contiguous + X via LDS.
+// k_unroll = RB (rows per batch), m_tile = 16*CT, k_split = KS; vector_width tells the
+// variants of one shape apart: 8 = rows strided over the grid, 9 = contiguous rows,
+// 10 = contiguous rows with X loaded first through LDS.
 #define MFMA_LDS_ENTRY(KS, RB, NB, CT, CONTIG, XL)                                                 \
     KernelEntry {                                                                                  \
-        skinny_config{SKINNY_PATH_MFMA_LDS, 64 * KS, RB * NB, RB, 8 + (CONTIG ? 1 : 0) + (XL ? 2 : 0), \
+        skinny_config{SKINNY_PATH_MFMA_LDS, 64 * KS, RB * NB, RB, XL ? 10 : (CONTIG ? 9 : 8),     \
                       16 * CT, KS},                                                                \
             &launch_mfma_lds<KS, RB, NB, CT, CONTIG, XL>,                                          \
             (const void *)&mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, false, false>,              \
@@ -222,20 +229,18 @@ int64_t lds_max_k() { return (int64_t)KS * 512; }
     }
 
 const KernelEntry kMfmaLdsEntries[] = {
-    MFMA_LDS_ENTRY(7, 16, 2, 1, false, false),
     MFMA_LDS_ENTRY(7, 16, 2, 1, true, false),
-    MFMA_LDS_ENTRY(7, 16, 2, 1, false, true),
     MFMA_LDS_ENTRY(7, 16, 2, 1, true, true),
-    MFMA_LDS_ENTRY(7, 16, 1, 1, false, false),
-    MFMA_LDS_ENTRY(7, 16, 1, 1, true, true),
-    MFMA_LDS_ENTRY(7, 16, 4, 1, false, false),
-    MFMA_LDS_ENTRY(7, 16, 4, 1, true, true),
-    MFMA_LDS_ENTRY(7, 8, 4, 1, false, false),
     MFMA_LDS_ENTRY(7, 8, 4, 1, true, true),
-    MFMA_LDS_ENTRY(7, 4, 7, 1, false, false),
+    MFMA_LDS_ENTRY(7, 8, 4, 1, true, false),
+    MFMA_LDS_ENTRY(7, 16, 2, 1, false, false),
+    MFMA_LDS_ENTRY(7, 16, 1, 1, true, false),
+    MFMA_LDS_ENTRY(7, 16, 4, 1, true, false),
+    MFMA_LDS_ENTRY(7, 16, 4, 1, true, true),
     MFMA_LDS_ENTRY(7, 4, 7, 1, true, true),
-    MFMA_LDS_ENTRY(7, 16, 2, 2, false, false),
+    MFMA_LDS_ENTRY(7, 16, 2, 2, true, false),
     MFMA_LDS_ENTRY(7, 16, 2, 2, true, true),
+    MFMA_LDS_ENTRY(7, 8, 4, 2, true, true),
 };
 
 }  // namespace

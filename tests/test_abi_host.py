@@ -122,6 +122,7 @@ def test_acc_needs_4_byte_alignment(L):
     ((0, 100, 4, 7, 8, 1, 1), 1),     # block not a multiple of 64
     ((0, 256, 0, 7, 8, 1, 1), 1),     # no outputs
     ((0, 256, 4, 7, 3, 1, 1), 1),     # vector width out of range
+    ((0, 256, 4, 7, 11, 1, 1), 1),    # vector width out of range
     ((0, 256, 4, 0, 8, 1, 1), 1),     # k_unroll 0
     ((0, 256, 4, 7, 8, -1, 1), 1),    # negative m tile
     ((0, 1024, 4, 7, 8, 1, 1), 3),    # well-formed but not built
