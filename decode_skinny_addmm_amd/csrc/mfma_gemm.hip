@@ -8,9 +8,10 @@
 //     of X) with 4 waves in a 2 x 2 layout, each wave a (BN/2) x (BM/2) block of
 //     v_mfma_f32_16x16x32_bf16 tiles;
 //   * K advances in stages of 128: both operand tiles are fetched with 16-byte loads, D
-//     stages ahead into registers so HBM latency is covered, then written
-//     to LDS (rows padded to 272 bytes: fragment reads hit distinct banks) and read back as
-//     A (W) and B (X^T) fragments;
+//     stages ahead into registers so HBM latency is covered, then written to one of two LDS
+//     buffers (rows padded to 272 bytes: fragment reads hit distinct banks) while the matrix
+//     cores work on the other, one barrier per stage, and read back as A (W) and B (X^T)
+//     fragments; larger wave blocks read less LDS per MFMA;
 //   * block ids are laid out so that the M-tiles of one W row tile are consecutive on the
 //     same XCD (blocks are dealt to the 8 XCDs round-robin): they run together and share
 //     the W tile through that XCD's L2, so W leaves HBM once;
@@ -46,10 +47,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     static_assert(LW >= 1 && LX >= 1 && TN >= 1 && TM >= 1, "tile too small");
     constexpr int STAGE_BYTES = (BN + BM) * kPitch;
     constexpr int CBYTES = BN * (BM + 4) * 4;        // fp32 block for the epilogue (padded)
-    constexpr int LDS_BYTES = STAGE_BYTES > CBYTES ? STAGE_BYTES : CBYTES;
+    constexpr int LDS_BYTES = 2 * STAGE_BYTES > CBYTES ? 2 * STAGE_BYTES : CBYTES;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    uint8_t *Ws = lds;
-    uint8_t *Xs = lds + BN * kPitch;
+    // stage buffer q: W tile at lds + q*STAGE_BYTES, X tile right after it
 
     // XCD-aware block order: block b runs on XCD b % 8; consecutive blocks of one XCD take
     // the m-tiles of one n-tile
@@ -85,6 +85,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
         }
     };
     auto stash = [&](int s, u32x4_t (&wr)[LW], u32x4_t (&xr)[LX]) {
+        uint8_t *Ws = lds + (s & 1) * STAGE_BYTES;
+        uint8_t *Xs = Ws + BN * kPitch;
         const bool kok = s * (kKC / 8) + lcol < KV;
 #pragma unroll
         for (int i = 0; i < LW; ++i)
@@ -103,9 +105,13 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     // The loop body is branch-free so the compiler keeps D stages of loads in flight (a
     // branch around a load makes it wait for every outstanding load): prefetches past the
     // last stage re-read the last stage (never used), stages past K are zero-filled.
+    // Stage s lives in LDS buffer s&1: during stage s the next stage is written to the other
+    // buffer while the matrix cores read this one, with one barrier per stage.
     u32x4_t wr[D][LW], xr[D][LX];
 #pragma unroll
     for (int d = 0; d < D; ++d) fetch(min(d, stages - 1), wr[d], xr[d]);
+    stash(0, wr[0], xr[0]);
+    fetch(min(D, stages - 1), wr[0], xr[0]);
 
     const int frow = lane & 15, fk = 16 * (lane >> 4);  // fragment row / byte offset in a k-step
     const int groups = (stages + D - 1) / D;
@@ -113,10 +119,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int s = g0 * D + d;
-            __syncthreads();                         // previous stage's fragment reads are done
-            stash(s, wr[d], xr[d]);
-            __syncthreads();
-            fetch(min(s + D, stages - 1), wr[d], xr[d]);
+            const int dn = (d + 1) % D;              // register slot of stage s + 1
+            __syncthreads();                         // stage s is in LDS; stage s-1 reads are done
+            stash(s + 1, wr[dn], xr[dn]);            // zero-filled when s + 1 is past K
+            fetch(min(s + 1 + D, stages - 1), wr[dn], xr[dn]);
+            const uint8_t *Ws = lds + (s & 1) * STAGE_BYTES;
+            const uint8_t *Xs = Ws + BN * kPitch;
             // each stage sums into a fresh tile that is then added to the total: the longest
             // fp32 rounding chain is 4 + K/128 steps instead of K/32
             f32x4_t st[TN][TM];
@@ -201,14 +209,13 @@ int64_t gemm_max_k() { return INT64_MAX; }
 
 const KernelEntry kGemmEntries[] = {
     GEMM_ENTRY(32, 32, 4),
-    GEMM_ENTRY(32, 32, 7),
     GEMM_ENTRY(32, 64, 4),
-    GEMM_ENTRY(32, 64, 2),
     GEMM_ENTRY(64, 64, 2),
     GEMM_ENTRY(64, 64, 4),
-    GEMM_ENTRY(32, 128, 2),
-    GEMM_ENTRY(32, 128, 4),
     GEMM_ENTRY(64, 128, 2),
+    GEMM_ENTRY(128, 64, 2),
+    GEMM_ENTRY(32, 128, 2),
+    GEMM_ENTRY(128, 128, 2),
     GEMM_ENTRY(32, 256, 2),
 };
 
