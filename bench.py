@@ -38,8 +38,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (published)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 
 
-def algorithmic_bytes(M: int, N: int = N_DIM, K: int = K_DIM) -> int:
+def algorithmic_bytes(M: int, N: int = None, K: int = None) -> int:
     """W read once, X read once, R read once, Y written once (bf16)."""
+    N = N_DIM if N is None else N
+    K = K_DIM if K is None else K
     return 2 * N * K + 2 * M * K + 2 * M * N + 2 * M * N
 
 
@@ -336,7 +338,7 @@ def measure(sk, wl, config, calls, warmup, steps):
     per, total_ms = time_graph(launch, wl, calls, warmup, steps)
     us_per_call = [p / calls for p in per]
     mean_us = total_ms * 1000.0 / (steps * calls)
-    gbs = algorithmic_bytes(wl.M) / (mean_us * 1e-6) / 1e9
+    gbs = algorithmic_bytes(wl.M, wl.N, wl.K) / (mean_us * 1e-6) / 1e9
     return launch, us_per_call, mean_us, gbs
 
 
@@ -396,15 +398,15 @@ def sweep_rows(args, sk, Ms, config_lists):
     out = open(args.out, "a") if args.out else None
     meta = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip}
     for M in Ms:
-        wl = Workload(M, args.copies)
+        wl = Workload(M, args.copies, args.n, args.k)
         for cfg in config_lists(M):
-            row = {"m": M, "n": N_DIM, "k": K_DIM, "config": cfg, "copies": args.copies,
+            row = {"m": M, "n": wl.N, "k": wl.K, "config": cfg, "copies": args.copies,
                    "calls": args.calls, **meta}
             try:
                 launch, samples, mean_us, gbs = measure(sk, wl, cfg, args.calls, args.warmup, args.steps)
                 row.update(summarize(samples))
                 row.update({"mean_us_total": mean_us, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                            "mfma_frac": 2.0 * M * N_DIM * K_DIM / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                            "mfma_frac": 2.0 * M * wl.N * wl.K / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                             "resources": sk.config_resources(cfg) if cfg.get("m_tile") else None,
                             "max_ulp_sampled": oracle_parity_sample(wl, launch, 256)})
             except Exception as e:  # noqa: BLE001
@@ -435,6 +437,8 @@ def main():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")
     p.add_argument("--ms", type=str, default=None, help="comma-separated M list for sweep/mcurve")
+    p.add_argument("--n", type=int, default=N_DIM, help="sweep/mcurve: N (rows of W); the default run uses 7168")
+    p.add_argument("--k", type=int, default=K_DIM, help="sweep/mcurve: K; the default run uses 3584")
     p.add_argument("--paths", type=str, default=None, help="sweep only these kernel paths (comma-separated ids)")
     p.add_argument("--with-torch", action="store_true",
                    help="mcurve: add torch.addmm (the vendor library) as a context row")
