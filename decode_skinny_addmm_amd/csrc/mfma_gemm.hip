@@ -5,8 +5,10 @@
 // the tens or hundreds, every workgroup can no longer hold all of X on chip, so this kernel
 // is a classic K-loop GEMM shaped for gfx950:
 //   * a workgroup computes a BN x BM block of Y^T (BN rows of W = output columns n, BM rows
-//     of X) with 4 waves in a 2 x 2 layout, each wave a (BN/2) x (BM/2) block of
-//     v_mfma_f32_16x16x32_bf16 tiles;
+//     of X) with KG groups of 4 waves; the waves of a group are in a 2 x 2 layout, each a
+//     (BN/2) x (BM/2) block of v_mfma_f32_16x16x32_bf16 tiles, and the KG groups take
+//     alternate K stages (more waves per CU when the grid is small), adding their partial
+//     blocks at the end;
 //   * K advances in stages of 128: both operand tiles are fetched with 16-byte loads, D
 //     stages ahead into registers so HBM latency is covered, then written to one of two LDS
 //     buffers (rows padded to 272 bytes: fragment reads hit distinct banks) while the matrix
@@ -34,9 +36,10 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// BN: rows of W per workgroup; BM: rows of X per workgroup; D: stages in flight.
-template <int BN, int BM, int D, bool ACC>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restrict__ X,
+// BN: rows of W per workgroup; BM: rows of X per workgroup; D: stages in flight per group;
+// KG: groups of 4 waves splitting the K stages.
+template <int BN, int BM, int D, int KG, bool ACC>
+__global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__restrict__ X,
                                                         const uint16_t *__restrict__ W,
                                                         const uint16_t *R, void *out,
                                                         int M, int N, int K, int n_tiles, int m_tiles) {
@@ -47,9 +50,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     static_assert(LW >= 1 && LX >= 1 && TN >= 1 && TM >= 1, "tile too small");
     constexpr int STAGE_BYTES = (BN + BM) * kPitch;
     constexpr int CBYTES = BN * (BM + 4) * 4;        // fp32 block for the epilogue (padded)
-    constexpr int LDS_BYTES = 2 * STAGE_BYTES > CBYTES ? 2 * STAGE_BYTES : CBYTES;
+    constexpr int LDS_BYTES = 2 * KG * STAGE_BYTES > CBYTES ? 2 * KG * STAGE_BYTES : CBYTES;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    // stage buffer q: W tile at lds + q*STAGE_BYTES, X tile right after it
+    // group kg, stage buffer q: W tile at lds + (2*kg + q)*STAGE_BYTES, X tile right after it
 
     // XCD-aware block order: block b runs on XCD b % 8; consecutive blocks of one XCD take
     // the m-tiles of one n-tile
@@ -60,19 +63,25 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     if (nt >= n_tiles) return;                       // padding block (uniform)
     const int n0 = nt * BN, m0 = mt * BM;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;               // thread within the group
+    const int kg = threadIdx.x >> 8;                 // K group: stages kg, kg + KG, ...
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wn = (wave & 1) * WN, wm = (wave >> 1) * WM;
     const int KV = K >> 3;                           // 16-byte vectors per row
     const int stages = (K + kKC - 1) / kKC;
+    const int gstages = (stages + KG - 1) / KG;      // stages of this group (some may be empty)
+    uint8_t *const glds = lds + 2 * kg * STAGE_BYTES;
     const u32x4_t *Wv = reinterpret_cast<const u32x4_t *>(W);
     const u32x4_t *Xv = reinterpret_cast<const u32x4_t *>(X);
 
     // thread -> (row, 16-byte column) of the stage tiles: 16 threads cover one 256-byte row
     const int lrow = tid >> 4, lcol = tid & 15;
+    // s below is the group-local stage; it covers the K stage s*KG + kg (stage numbers at or
+    // past `stages` are empty and zero-filled)
+    auto kstage = [&](int s) { return s * KG + kg; };
     auto fetch = [&](int s, u32x4_t (&wr)[LW], u32x4_t (&xr)[LX]) {
-        const int v = min(s * (kKC / 8) + lcol, KV - 1);   // clamped; zeroed below if past K
+        const int v = min(kstage(s) * (kKC / 8) + lcol, KV - 1);  // clamped; zeroed if past K
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
             const int n = min(n0 + lrow + 16 * i, N - 1);
@@ -85,9 +94,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
         }
     };
     auto stash = [&](int s, u32x4_t (&wr)[LW], u32x4_t (&xr)[LX]) {
-        uint8_t *Ws = lds + (s & 1) * STAGE_BYTES;
+        uint8_t *Ws = glds + (s & 1) * STAGE_BYTES;
         uint8_t *Xs = Ws + BN * kPitch;
-        const bool kok = s * (kKC / 8) + lcol < KV;
+        const bool kok = kstage(s) * (kKC / 8) + lcol < KV;
 #pragma unroll
         for (int i = 0; i < LW; ++i)
             *reinterpret_cast<u32x4_t *>(Ws + (lrow + 16 * i) * kPitch + 16 * lcol) = kok ? wr[i] : u32x4_t{};
@@ -109,12 +118,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     // buffer while the matrix cores read this one, with one barrier per stage.
     u32x4_t wr[D][LW], xr[D][LX];
 #pragma unroll
-    for (int d = 0; d < D; ++d) fetch(min(d, stages - 1), wr[d], xr[d]);
+    for (int d = 0; d < D; ++d) fetch(min(d, gstages - 1), wr[d], xr[d]);
     stash(0, wr[0], xr[0]);
-    fetch(min(D, stages - 1), wr[0], xr[0]);
+    fetch(min(D, gstages - 1), wr[0], xr[0]);
 
     const int frow = lane & 15, fk = 16 * (lane >> 4);  // fragment row / byte offset in a k-step
-    const int groups = (stages + D - 1) / D;
+    const int groups = (gstages + D - 1) / D;
     for (int g0 = 0; g0 < groups; ++g0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -122,8 +131,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
             const int dn = (d + 1) % D;              // register slot of stage s + 1
             __syncthreads();                         // stage s is in LDS; stage s-1 reads are done
             stash(s + 1, wr[dn], xr[dn]);            // zero-filled when s + 1 is past K
-            fetch(min(s + 1 + D, stages - 1), wr[dn], xr[dn]);
-            const uint8_t *Ws = lds + (s & 1) * STAGE_BYTES;
+            fetch(min(s + 1 + D, gstages - 1), wr[dn], xr[dn]);
+            const uint8_t *Ws = glds + (s & 1) * STAGE_BYTES;
             const uint8_t *Xs = Ws + BN * kPitch;
             // each stage sums into a fresh tile that is then added to the total: the longest
             // fp32 rounding chain is 4 + K/128 steps instead of K/32
@@ -154,19 +163,27 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     }
 
     // epilogue: acc[a][c][r] = Y^T[n0 + wn + 16a + 4*(lane/16) + r][m0 + wm + 16c + lane%16]
+    // (partial over this group's stages); the groups add into C in group order
     __syncthreads();
     float *C = reinterpret_cast<float *>(lds);       // C[n][m], row pitch BM + 4 floats
 #pragma unroll
-    for (int a = 0; a < TN; ++a)
+    for (int q = 0; q < KG; ++q) {
+        if (kg == q) {
 #pragma unroll
-        for (int c = 0; c < TM; ++c)
+            for (int a = 0; a < TN; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                C[(wn + 16 * a + 4 * (lane >> 4) + r) * (BM + 4) + wm + 16 * c + (lane & 15)] = acc[a][c][r];
-    __syncthreads();
+                for (int c = 0; c < TM; ++c)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float &slot = C[(wn + 16 * a + 4 * (lane >> 4) + r) * (BM + 4) + wm + 16 * c + (lane & 15)];
+                        slot = (q == 0) ? acc[a][c][r] : slot + acc[a][c][r];
+                    }
+        }
+        __syncthreads();
+    }
     // walk the block row by row of Y: neighbouring threads take neighbouring n
 #pragma unroll 4
-    for (int e = tid; e < BN * BM; e += 256) {
+    for (int e = threadIdx.x; e < BN * BM; e += 256 * KG) {
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
@@ -180,43 +197,45 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(const uint16_t *__restri
     }
 }
 
-template <int BN, int BM, int D>
+template <int BN, int BM, int D, int KG>
 hipError_t launch_gemm(const LaunchArgs &a) {
     const int n_tiles = (int)((a.N + BN - 1) / BN);
     const int m_tiles = (int)((a.M + BM - 1) / BM);
     const int groups = (n_tiles + 7) / 8;            // n-tiles per XCD, rounded up
     dim3 grid((unsigned)(groups * 8 * m_tiles));
-    dim3 block(256);
+    dim3 block(256 * KG);
     if (a.acc_out)
-        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
+        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, KG, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
                            (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
     else
-        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
+        hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, KG, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
                            (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
     return hipGetLastError();
 }
 
 int64_t gemm_max_k() { return INT64_MAX; }
 
-// Public knobs: path SKINNY_PATH_GEMM, block_size 256, outputs_per_block = BN,
-// k_unroll = D (stages in flight), vector_width = 8, m_tile = BM, k_split = 1.
-#define GEMM_ENTRY(BN, BM, D)                                                                      \
+// Public knobs: path SKINNY_PATH_GEMM, block_size = 256*KG, outputs_per_block = BN,
+// k_unroll = D (stages in flight per group), vector_width = 8, m_tile = BM, k_split = KG
+// (groups of 4 waves; a wave's block is fixed by BN, BM).
+#define GEMM_ENTRY(BN, BM, D, KG)                                                                  \
     KernelEntry {                                                                                  \
-        skinny_config{SKINNY_PATH_GEMM, 256, BN, D, 8, BM, 1}, &launch_gemm<BN, BM, D>,            \
-            (const void *)&mfma_gemm_kernel<BN, BM, D, false>,                                     \
-            (const void *)&mfma_gemm_kernel<BN, BM, D, true>, &gemm_max_k                          \
+        skinny_config{SKINNY_PATH_GEMM, 256 * KG, BN, D, 8, BM, KG}, &launch_gemm<BN, BM, D, KG>,  \
+            (const void *)&mfma_gemm_kernel<BN, BM, D, KG, false>,                                 \
+            (const void *)&mfma_gemm_kernel<BN, BM, D, KG, true>, &gemm_max_k                      \
     }
 
 const KernelEntry kGemmEntries[] = {
-    GEMM_ENTRY(32, 32, 4),
-    GEMM_ENTRY(32, 64, 4),
-    GEMM_ENTRY(64, 64, 2),
-    GEMM_ENTRY(64, 64, 4),
-    GEMM_ENTRY(64, 128, 2),
-    GEMM_ENTRY(128, 64, 2),
-    GEMM_ENTRY(32, 128, 2),
-    GEMM_ENTRY(128, 128, 2),
-    GEMM_ENTRY(32, 256, 2),
+    GEMM_ENTRY(32, 32, 4, 1),
+    GEMM_ENTRY(32, 64, 4, 1),
+    GEMM_ENTRY(64, 64, 4, 1),
+    GEMM_ENTRY(64, 64, 2, 1),
+    GEMM_ENTRY(64, 128, 2, 1),
+    GEMM_ENTRY(32, 32, 2, 2),
+    GEMM_ENTRY(32, 64, 2, 2),
+    GEMM_ENTRY(32, 64, 4, 2),
+    GEMM_ENTRY(64, 64, 2, 2),
+    GEMM_ENTRY(64, 64, 4, 2),
 };
 
 }  // namespace

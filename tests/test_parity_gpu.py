@@ -123,6 +123,25 @@ def test_every_config_full_size_sampled(sk, M):
         P.check_acc(Ag[ms, ns], ao, "M=%d %s" % (M, cfg))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 4104), (4, 256, 8), (16, 200, 9000), (64, 130, 24),
+                                   (300, 1000, 1032), (257, 515, 3584), (33, 70, 512)])
+def test_selected_config_any_shape(sk, M, N, K):
+    """The library's own choice (tuned table, with its fallbacks for other K) at shapes off the
+    tuned one: ragged N, K outside a kernel's on-chip slice, M above the table."""
+    X, ws, rs = synth.make_inputs(M, N, K, seed=M + N + K)
+    print("selected config", (M, N, K), sk.select_config(M, N, K), flush=True)
+    Xd, Wd, Rd = _dev(X, ws[0], rs[0])
+    Y = sk.addmm_default(Xd, Wd, Rd, torch.empty_like(Rd))
+    A = sk.addmm_acc_f32(Xd, Wd, Rd)
+    torch.cuda.synchronize()
+    Yg, Ag = P.bits_of(Y), A.cpu().numpy()
+    ms, ns = sample_positions(M, N, 1500, K)
+    yo, ao = oracle.addmm_bf16_points(synth.bits(X), synth.bits(ws[0]), synth.bits(rs[0]), ms, ns)
+    P.check_y(Yg[ms, ns], yo, ao, "selected %s" % ((M, N, K),))
+    P.check_acc(Ag[ms, ns], ao, "selected %s" % ((M, N, K),))
+    assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
+
+
 # ------------------------------------------------------------------ exact cases (bit-exact)
 
 @pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (3, 77, 264)])
@@ -181,8 +200,8 @@ def test_empty_m_and_n_are_noops(sk):
     assert sk.addmm(X, W, R).shape == (2, 0)
 
 
-def test_in_place_residual(sk):
-    M = 4
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 256])
+def test_in_place_residual(sk, M):
     X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL)
     Xd, Wd, Rd = _dev(X, ws[0], rs[0])
     Y = sk.addmm(Xd, Wd, Rd)
@@ -193,7 +212,7 @@ def test_in_place_residual(sk):
 
 
 def test_poisoned_output_fully_written(sk):
-    for M in (1, 5, 16, 33):
+    for M in (1, 2, 5, 16, 33, 100, 257):
         X, ws, rs = synth.make_inputs(M, 1000, 1024)
         Xd, Wd, Rd = _dev(X, ws[0], rs[0])
         Y = torch.full_like(Rd, float("nan"))
