@@ -395,6 +395,7 @@ def run_default(args, sk):
 
 def sweep_rows(args, sk, Ms, config_lists):
     import torch
+    from decode_skinny_addmm_amd._lib import PATH_SIMT
     out = open(args.out, "a") if args.out else None
     meta = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip}
     for M in Ms:
@@ -402,6 +403,11 @@ def sweep_rows(args, sk, Ms, config_lists):
         for cfg in config_lists(M):
             row = {"m": M, "n": wl.N, "k": wl.K, "config": cfg, "copies": args.copies,
                    "calls": args.calls, **meta}
+            if cfg.get("path") == PATH_SIMT:
+                # the pages' kernels need K to be a whole number of block_size*vector_width
+                # tiles, k_unroll at a time; this family takes a predicated tail instead
+                tile = cfg["block_size"] * cfg["vector_width"]
+                row["tail_free"] = wl.K % tile == 0 and (wl.K // tile) % cfg["k_unroll"] == 0
             try:
                 launch, samples, mean_us, gbs = measure(sk, wl, cfg, args.calls, args.warmup, args.steps)
                 row.update(summarize(samples))

@@ -14,6 +14,7 @@ PATH_GEMV = 0
 PATH_MFMA = 1
 PATH_MFMA_LDS = 2
 PATH_GEMM = 3
+PATH_SIMT = 4
 CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",

@@ -26,6 +26,8 @@ struct Registry {
         for (int i = 0; i < n; ++i) all.push_back(&l[i]);
         const KernelEntry *t = gemm_entries(&n);
         for (int i = 0; i < n; ++i) all.push_back(&t[i]);
+        const KernelEntry *s = simt_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&s[i]);
     }
 };
 

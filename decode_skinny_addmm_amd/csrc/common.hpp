@@ -37,6 +37,7 @@ const KernelEntry *gemv_entries(int *count);
 const KernelEntry *mfma_entries(int *count);
 const KernelEntry *mfma_lds_entries(int *count);
 const KernelEntry *gemm_entries(int *count);
+const KernelEntry *simt_entries(int *count);
 
 // ----------------------------------------------------------------------------- device helpers
 

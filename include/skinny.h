@@ -60,8 +60,13 @@ enum {
     SKINNY_PATH_MFMA = 1, /* matrix-core path, fragments loaded straight from memory; any K */
     SKINNY_PATH_MFMA_LDS = 2, /* matrix-core path, W streamed in 1 KB row pieces and turned
                                  into fragments through LDS; K <= 512 * k_split */
-    SKINNY_PATH_GEMM = 3      /* matrix-core K-loop GEMM with LDS-staged operand tiles, for
+    SKINNY_PATH_GEMM = 3,     /* matrix-core K-loop GEMM with LDS-staged operand tiles, for
                                  larger M; any K */
+    SKINNY_PATH_SIMT = 4      /* the vLLM API page's SIMT decomposition, knobs taken as named:
+                                 thread t of a block_size workgroup takes vector t of every
+                                 block_size * vector_width K-tile of outputs_per_block W rows,
+                                 k_unroll tiles per step, X loaded through the cache; any K.
+                                 Built for the page-1 sweep grid at m_tile 16 */
 };
 
 /*
@@ -75,7 +80,11 @@ typedef struct skinny_config {
     int32_t outputs_per_block; /* output columns (rows of W) per workgroup */
     int32_t k_unroll;          /* GEMV: vectors of one W row in flight per lane per step;
                                   MFMA: 32-wide K steps in flight per wave */
-    int32_t vector_width;      /* bf16 elements per W load per lane: 8 (16 B) or 4 (8 B) */
+    int32_t vector_width;      /* bf16 elements per W load per lane: 8 (16 B) or, SIMT only,
+                                  4 (8 B). GEMV and MFMA_LDS encode their row order here:
+                                  8 = rows strided over the grid, 9 = contiguous rows per
+                                  workgroup, 10 (MFMA_LDS) = contiguous with X loaded first;
+                                  all three load 16 B */
     int32_t m_tile;            /* rows of X handled per pass (compile-time tile); M larger
                                   than m_tile runs ceil(M / m_tile) passes; 0 = let the
                                   library pick the smallest built tile >= M */
