@@ -15,6 +15,7 @@ PATH_MFMA = 1
 PATH_MFMA_LDS = 2
 PATH_GEMM = 3
 PATH_SIMT = 4
+PATH_GEMM_DMA = 5
 CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",

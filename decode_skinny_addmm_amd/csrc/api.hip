@@ -28,6 +28,8 @@ struct Registry {
         for (int i = 0; i < n; ++i) all.push_back(&t[i]);
         const KernelEntry *s = simt_entries(&n);
         for (int i = 0; i < n; ++i) all.push_back(&s[i]);
+        const KernelEntry *d = dma_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&d[i]);
     }
 };
 
@@ -70,11 +72,12 @@ skinny_config table_row(int64_t M) {
 }
 
 // The table's choice for M, unless that kernel cannot take this K (GEMV instances hold
-// their K slice in registers); then the general MFMA configuration, which loops over K.
+// their K slice in registers; the direct-to-LDS GEMM needs whole 128-wide K stages); then
+// the general configuration for that M range, which takes any K.
 skinny_config select(int64_t M, int64_t K) {
     const skinny_config c = table_row(M);
     const KernelEntry *e = find_entry(c, M);
-    if (e && K <= e->max_k()) return c;
+    if (e && K <= e->max_k() && K % e->k_align == 0) return c;
     return M <= 16 ? kFallbackSmall : kFallbackLarge;
 }
 
@@ -99,7 +102,7 @@ skinny_status run(const void *X, const void *W, const void *R, void *out, bool a
         return SKINNY_EINVAL;
     const KernelEntry *e = find_entry(c, M);
     if (!e) return SKINNY_ENOTSUP;
-    if (K > e->max_k()) return SKINNY_ENOTSUP;
+    if (K > e->max_k() || K % e->k_align != 0) return SKINNY_ENOTSUP;
     // K == 0 (Y = R): all kernels but the direct MFMA one issue their first loads unconditionally, so the empty
     // sum goes to the general kernel, whose K loop simply does not run.
     if (K == 0 && e->cfg.path != SKINNY_PATH_MFMA)

@@ -30,6 +30,7 @@ struct KernelEntry {
     const void *fn_bf16;            // kernel writing bf16 Y
     const void *fn_acc;             // kernel writing fp32 ACC
     int64_t (*max_k)();             // largest K the instance accepts (LDS limits), or INT64_MAX
+    int32_t k_align = 8;            // K must be a multiple of this
 };
 
 // Registries filled by each kernel family's translation unit.
@@ -38,6 +39,7 @@ const KernelEntry *mfma_entries(int *count);
 const KernelEntry *mfma_lds_entries(int *count);
 const KernelEntry *gemm_entries(int *count);
 const KernelEntry *simt_entries(int *count);
+const KernelEntry *dma_entries(int *count);
 
 // ----------------------------------------------------------------------------- device helpers
 

@@ -17,8 +17,9 @@
 //   * block ids are laid out so that the M-tiles of one W row tile are consecutive on the
 //     same XCD (blocks are dealt to the 8 XCDs round-robin): they run together and share
 //     the W tile through that XCD's L2, so W leaves HBM once;
-//   * the epilogue stages the fp32 block in LDS and walks it row by row of Y, so residual
-//     loads and output stores are contiguous; R is added in fp32, one RNE rounding to bf16.
+//   * R is fetched into registers at the start (its latency hides behind the K loop); the
+//     epilogue stages the fp32 block in LDS and walks it row by row of Y, so residual loads
+//     and output stores are contiguous; R is added in fp32, one RNE rounding to bf16.
 #include "common.hpp"
 
 namespace skinny {
@@ -105,6 +106,18 @@ __global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__r
             *reinterpret_cast<u32x4_t *>(Xs + (lrow + 16 * i) * kPitch + 16 * lcol) = kok ? xr[i] : u32x4_t{};
     };
 
+    // residual prefetch: thread t finishes elements e = t + 256*KG*i of the block, taken row by
+    // row of Y (ml = e / BN, nl = e % BN); clamped addresses keep the loads unconditional, and
+    // their latency hides behind the K loop
+    constexpr int EPT = BN * BM / (256 * KG);
+    static_assert(EPT * 256 * KG == BN * BM, "epilogue split");
+    uint16_t rv[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + 256 * KG * i;
+        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * N + min(n0 + e % BN, N - 1)];
+    }
+
     f32x4_t acc[TN][TM];
 #pragma unroll
     for (int a = 0; a < TN; ++a)
@@ -182,13 +195,14 @@ __global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__r
         __syncthreads();
     }
     // walk the block row by row of Y: neighbouring threads take neighbouring n
-#pragma unroll 4
-    for (int e = threadIdx.x; e < BN * BM; e += 256 * KG) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + 256 * KG * i;
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
             const size_t o = (size_t)m * N + n;
-            const float y = C[nl * (BM + 4) + ml] + bf16_bits_to_f32(R[o]);
+            const float y = C[nl * (BM + 4) + ml] + bf16_bits_to_f32(rv[i]);
             if constexpr (ACC)
                 static_cast<float *>(out)[o] = y;
             else

@@ -62,11 +62,14 @@ enum {
                                  into fragments through LDS; K <= 512 * k_split */
     SKINNY_PATH_GEMM = 3,     /* matrix-core K-loop GEMM with LDS-staged operand tiles, for
                                  larger M; any K */
-    SKINNY_PATH_SIMT = 4      /* the vLLM API page's SIMT decomposition, knobs taken as named:
+    SKINNY_PATH_SIMT = 4,     /* the vLLM API page's SIMT decomposition, knobs taken as named:
                                  thread t of a block_size workgroup takes vector t of every
                                  block_size * vector_width K-tile of outputs_per_block W rows,
                                  k_unroll tiles per step, X loaded through the cache; any K.
                                  Built for the page-1 sweep grid at m_tile 16 */
+    SKINNY_PATH_GEMM_DMA = 5  /* matrix-core K-loop GEMM whose operand tiles are loaded from
+                                 memory straight into a ring of LDS stages (k_unroll = stages);
+                                 K must be a multiple of 128 (else SKINNY_ENOTSUP) */
 };
 
 /*

@@ -49,7 +49,7 @@ def test_select_config_covers_all_m(L):
         c = _lib.SkinnyConfig()
         assert L.skinny_select_config(M, 7168, 3584, ctypes.byref(c)) == 0
         d = c.as_dict()
-        assert d["block_size"] % 64 == 0 and d["m_tile"] >= 1 and d["path"] in (0, 1, 2, 3, 4)
+        assert d["block_size"] % 64 == 0 and d["m_tile"] >= 1 and d["path"] in (0, 1, 2, 3, 4, 5)
         seen.add(tuple(d.values()))
     # every selected configuration is built into the library
     built = set()
@@ -126,7 +126,7 @@ def test_acc_needs_4_byte_alignment(L):
     ((0, 256, 4, 0, 8, 1, 1), 1),     # k_unroll 0
     ((0, 256, 4, 7, 8, -1, 1), 1),    # negative m tile
     ((0, 1024, 4, 7, 8, 1, 1), 3),    # well-formed but not built
-    ((5, 256, 4, 7, 8, 1, 1), 3),     # unknown path
+    ((9, 256, 4, 7, 8, 1, 1), 3),     # unknown path
 ])
 def test_config_checks(L, cfg, expect):
     c = _lib.SkinnyConfig(*cfg)

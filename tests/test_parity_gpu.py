@@ -41,11 +41,20 @@ def full_oracle(X, W, R):
 
 
 SMALL_SHAPES = [(1, 64, 512), (3, 100, 1032), (5, 33, 3584), (8, 130, 776), (16, 257, 520),
-                (17, 70, 264), (2, 1, 8), (4, 96, 4096 + 8), (1, 3, 24), (2, 20, 9000)]
+                (17, 70, 264), (2, 1, 8), (4, 96, 4096 + 8), (1, 3, 24), (2, 20, 9000),
+                (33, 70, 256), (65, 130, 1024), (130, 200, 384), (64, 64, 128)]
 
 
-def all_configs(sk):
-    return sk.configs()
+def refuses(cfg, K):
+    """Instances that must refuse this K with SKINNY_ENOTSUP: GEMV and LDS-MFMA hold their K
+    slice on chip; the direct-to-LDS GEMM takes whole 128-wide K stages only."""
+    return ((cfg["path"] == 0 and K > cfg["k_unroll"] * cfg["k_split"] * 512) or
+            (cfg["path"] == 2 and K > cfg["k_split"] * 512) or
+            (cfg["path"] == 5 and K % 128 != 0))
+
+
+def all_configs(sk, K=None):
+    return [c for c in sk.configs() if K is None or not refuses(c, K)]
 
 
 def test_small_shapes_every_config(sk):
@@ -54,10 +63,7 @@ def test_small_shapes_every_config(sk):
         Yo, Ao = full_oracle(X, ws[0], rs[0])
         for cfg in all_configs(sk):
             print("small shape", (M, N, K), "config", cfg, flush=True)
-            too_long = ((cfg["path"] == 0 and K > cfg["k_unroll"] * cfg["k_split"] * 512) or
-                        (cfg["path"] == 2 and K > cfg["k_split"] * 512))
-            if too_long:
-                # GEMV and LDS-MFMA instances hold their K slice on chip: larger K is refused
+            if refuses(cfg, K):
                 with pytest.raises(sk.ops.SkinnyError) as ei:
                     run_both(sk, X, ws[0], rs[0], cfg)
                 assert ei.value.status == 3
@@ -123,6 +129,23 @@ def test_every_config_full_size_sampled(sk, M):
         P.check_acc(Ag[ms, ns], ao, "M=%d %s" % (M, cfg))
 
 
+@pytest.mark.parametrize("M", [64, 256])
+def test_matrix_core_configs_full_size_sampled(sk, M):
+    """Every matrix-core K-loop instance (direct MFMA, GEMM, direct-to-LDS GEMM) at the full
+    problem size and large M: sampled outputs against the oracle."""
+    X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL)
+    ms, ns = sample_positions(M, N_FULL, 2000, 200 + M)
+    yo, ao = oracle.addmm_bf16_points(synth.bits(X), synth.bits(ws[0]), synth.bits(rs[0]), ms, ns)
+    for cfg in all_configs(sk, K_FULL):
+        if cfg["path"] not in (1, 3, 5):
+            continue
+        print("full size M=%d config %s" % (M, cfg), flush=True)
+        Yg, Ag = run_both(sk, X, ws[0], rs[0], cfg)
+        P.check_y(Yg[ms, ns], yo, ao, "M=%d %s" % (M, cfg))
+        P.check_acc(Ag[ms, ns], ao, "M=%d %s" % (M, cfg))
+        assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 300, 4104), (4, 256, 8), (16, 200, 9000), (64, 130, 24),
                                    (300, 1000, 1032), (257, 515, 3584), (33, 70, 512)])
 def test_selected_config_any_shape(sk, M, N, K):
@@ -144,34 +167,34 @@ def test_selected_config_any_shape(sk, M, N, K):
 
 # ------------------------------------------------------------------ exact cases (bit-exact)
 
-@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (3, 77, 264)])
+@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (3, 77, 264), (70, 150, 640)])
 def test_x_zero_gives_r(sk, M, N, K):
     _, ws, rs = synth.make_inputs(M, N, K)
     X = torch.zeros((M, K), dtype=torch.bfloat16)
-    for cfg in [None] + all_configs(sk):
+    for cfg in [None] + all_configs(sk, K):
         Yg, _ = run_both(sk, X, ws[0], rs[0], cfg)
         Rb = synth.bits(rs[0])
         same = (Yg == Rb) | (((Yg & 0x7FFF) == 0) & ((Rb & 0x7FFF) == 0))
         assert same.all(), cfg
 
 
-@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (16, 130, 520)])
+@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (16, 130, 520), (70, 150, 640)])
 def test_one_hot_rows(sk, M, N, K):
     X, _, rs = synth.make_inputs(M, N, K, seed=21)
     cols = (np.arange(N) * 131 + 7) % K
     W = synth.one_hot_rows(N, K, cols)
     Yo, Ao = full_oracle(X, W, rs[0])
-    for cfg in [None] + all_configs(sk):
+    for cfg in [None] + all_configs(sk, K):
         Yg, Ag = run_both(sk, X, W, rs[0], cfg)
         assert np.array_equal(Yg, Yo), cfg
         assert np.array_equal(Ag.astype(np.float64), Ao), cfg
 
 
-@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (8, 100, 1032)])
+@pytest.mark.parametrize("M,N,K", [(4, N_FULL, K_FULL), (8, 100, 1032), (40, 100, 1024)])
 def test_small_integers_exact(sk, M, N, K):
     X, W, R = synth.small_int_inputs(M, N, K)
     Yo, Ao = full_oracle(X, W, R)
-    for cfg in [None] + all_configs(sk):
+    for cfg in [None] + all_configs(sk, K):
         Yg, Ag = run_both(sk, X, W, R, cfg)
         assert np.array_equal(Ag.astype(np.float64), Ao), cfg
         assert np.array_equal(Yg, Yo), cfg
