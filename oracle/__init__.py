@@ -3,8 +3,9 @@
 Plain fp64 definition of the skinny residual GEMM (bf16 X[M,K], W[N,K],
 R[M,N]; one round-to-nearest-even to bf16), written from the vLLM benchmark
 page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py" (module docstring
-and its torch.addmm leg). The arithmetic lives in ``oracle.c``; this module
-only builds it with gcc and marshals numpy arrays.
+and its torch.addmm leg), plus the shard epilogue of the vLLM API page
+"fused_add_multicast_skinny_gemm" behind two flags. The arithmetic lives in
+``oracle.c``; this module only builds it with gcc and marshals numpy arrays.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. It shares no code with the GPU library
@@ -25,6 +26,12 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _default = None
+
+# Epilogue options of the page-2 shard form (the vLLM API page
+# "fused_add_multicast_skinny_gemm"): round the product sum to bf16 before adding the
+# residual (two roundings), and write +0 for a -0 result.
+ROUND_PRODUCT = 1
+NO_NEG_ZERO = 2
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -65,18 +72,21 @@ class Oracle:
         f64p = ctypes.POINTER(ctypes.c_double)
         i64p = ctypes.POINTER(ctypes.c_int64)
         i64 = ctypes.c_int64
-        lib.oracle_addmm_bf16.argtypes = [u16p, u16p, u16p, u16p, f64p, i64, i64, i64, ctypes.c_int]
-        lib.oracle_addmm_bf16.restype = ctypes.c_int
-        lib.oracle_addmm_bf16_points.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64p, i64p, i64,
-                                                 u16p, f64p]
-        lib.oracle_addmm_bf16_points.restype = ctypes.c_int
+        u32 = ctypes.c_uint
+        lib.oracle_addmm_bf16_ex.argtypes = [u16p, u16p, u16p, u16p, f64p, i64, i64, i64, u32, ctypes.c_int]
+        lib.oracle_addmm_bf16_ex.restype = ctypes.c_int
+        lib.oracle_addmm_bf16_points_ex.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64p, i64p, i64,
+                                                    u32, u16p, f64p]
+        lib.oracle_addmm_bf16_points_ex.restype = ctypes.c_int
         lib.oracle_round_bf16_array.argtypes = [f64p, u16p, i64]
         lib.oracle_round_bf16_array.restype = None
         self.lib = lib
         self.path = path
 
-    def addmm_bf16(self, X, W, R, threads: int | None = None, want_acc: bool = True):
-        """Return (Y bits uint16[M,N], exact fp64 sums float64[M,N] or None)."""
+    def addmm_bf16(self, X, W, R, threads: int | None = None, want_acc: bool = True, flags: int = 0):
+        """Return (Y bits uint16[M,N], exact fp64 sums float64[M,N] or None). flags: ROUND_PRODUCT
+        and/or NO_NEG_ZERO (the page-2 epilogue); with ROUND_PRODUCT the second array holds
+        bf16(sum) + r, the value of the second rounding."""
         X = _u16(X)
         W = _u16(W)
         if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
@@ -86,15 +96,15 @@ class Oracle:
         R = _u16(R, (M, N))
         Y = np.empty((M, N), dtype=np.uint16)
         ACC = np.empty((M, N), dtype=np.float64) if want_acc else None
-        rc = self.lib.oracle_addmm_bf16(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
-                                        _ptr(R, ctypes.c_uint16), _ptr(Y, ctypes.c_uint16),
-                                        _ptr(ACC, ctypes.c_double) if ACC is not None else None,
-                                        M, N, K, int(threads or default_threads()))
+        rc = self.lib.oracle_addmm_bf16_ex(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
+                                           _ptr(R, ctypes.c_uint16), _ptr(Y, ctypes.c_uint16),
+                                           _ptr(ACC, ctypes.c_double) if ACC is not None else None,
+                                           M, N, K, int(flags), int(threads or default_threads()))
         if rc != 0:
             raise RuntimeError("oracle_addmm_bf16 failed (%d)" % rc)
         return Y, ACC
 
-    def addmm_bf16_points(self, X, W, R, ms, ns):
+    def addmm_bf16_points(self, X, W, R, ms, ns, flags: int = 0):
         """Oracle values at the listed (m, n): (Y bits uint16[c], fp64 sums float64[c])."""
         X = _u16(X)
         W = _u16(W)
@@ -108,10 +118,11 @@ class Oracle:
         c = ms.shape[0]
         Y = np.empty(c, dtype=np.uint16)
         ACC = np.empty(c, dtype=np.float64)
-        rc = self.lib.oracle_addmm_bf16_points(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
-                                               _ptr(R, ctypes.c_uint16), M, N, K,
-                                               _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64), c,
-                                               _ptr(Y, ctypes.c_uint16), _ptr(ACC, ctypes.c_double))
+        rc = self.lib.oracle_addmm_bf16_points_ex(_ptr(X, ctypes.c_uint16), _ptr(W, ctypes.c_uint16),
+                                                  _ptr(R, ctypes.c_uint16), M, N, K,
+                                                  _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64), c,
+                                                  int(flags), _ptr(Y, ctypes.c_uint16),
+                                                  _ptr(ACC, ctypes.c_double))
         if rc != 0:
             raise ValueError("point index out of range")
         return Y, ACC
@@ -133,12 +144,12 @@ def default() -> Oracle:
     return _default
 
 
-def addmm_bf16(X, W, R, threads: int | None = None, want_acc: bool = True):
-    return default().addmm_bf16(X, W, R, threads=threads, want_acc=want_acc)
+def addmm_bf16(X, W, R, threads: int | None = None, want_acc: bool = True, flags: int = 0):
+    return default().addmm_bf16(X, W, R, threads=threads, want_acc=want_acc, flags=flags)
 
 
-def addmm_bf16_points(X, W, R, ms, ns):
-    return default().addmm_bf16_points(X, W, R, ms, ns)
+def addmm_bf16_points(X, W, R, ms, ns, flags: int = 0):
+    return default().addmm_bf16_points(X, W, R, ms, ns, flags=flags)
 
 
 def round_bf16(v) -> np.ndarray:

@@ -25,6 +25,17 @@
  *  - round-to-nearest, ties-to-even; NaN stays NaN; overflow goes to +-Inf;
  *  - no sanitising of negative zero.
  *
+ * The page-2 epilogue itself (the vLLM API page "fused_add_multicast_skinny_gemm",
+ * FusedAddMulticastSkinnyGemm.kernel, tensor-parallel shard form) is available through
+ * the *_ex entry points and two flags:
+ *  - ORACLE_ROUND_PRODUCT: g = bf16(sum_k x*w) first, then Y = bf16(g + r). g and r are
+ *    bf16 values, so g + r is exact in fp64 whenever their exponents differ by at most
+ *    45; otherwise the smaller one is below 2^-45 of the larger and cannot move the
+ *    bf16 rounding of the sum, so fp64 gives the exact rounded result either way;
+ *  - ORACLE_NO_NEG_ZERO: a bf16 result of -0 is written as +0 (that page keeps -0 as
+ *    its not-yet-written marker).
+ * With no flag the *_ex functions compute exactly what the plain ones do.
+ *
  * Who may use this: only the test suite, the package smoke check and the
  * benchmark's CPU-baseline leg. The GPU library never links or calls it, and
  * this file includes nothing from the GPU library.
@@ -82,12 +93,19 @@ uint16_t oracle_round_bf16(double v) {
     return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
 }
 
-/* One output element, by the definition above. */
+#define ORACLE_ROUND_PRODUCT 1u
+#define ORACLE_NO_NEG_ZERO 2u
+
+/* One output element, by the definition above. With ORACLE_ROUND_PRODUCT the residual is
+ * left out of the compensated sum and added after the sum has been rounded to bf16; acc_out
+ * then receives bf16(sum) + r, the value the second rounding applies to. */
 static void one_element(const uint16_t *X, const uint16_t *W, const uint16_t *R,
-                        int64_t N, int64_t K, int64_t m, int64_t n,
+                        int64_t N, int64_t K, int64_t m, int64_t n, unsigned flags,
                         uint16_t *y_out, double *acc_out) {
+    const int round_product = (flags & ORACLE_ROUND_PRODUCT) != 0;
     double s = 0.0, c = 0.0;      /* Neumaier: running sum and compensation */
     for (int64_t k = 0; k <= K; ++k) {
+        if (k == K && round_product) break;
         double p = (k < K) ? bf16_bits_to_double(X[m * K + k]) * bf16_bits_to_double(W[n * K + k])
                            : bf16_bits_to_double(R[m * N + n]);
         double t = s + p;
@@ -96,8 +114,14 @@ static void one_element(const uint16_t *X, const uint16_t *W, const uint16_t *R,
         s = t;
     }
     double exact = s + c;
+    if (round_product)
+        exact = bf16_bits_to_double(oracle_round_bf16(exact)) + bf16_bits_to_double(R[m * N + n]);
     if (acc_out) *acc_out = exact;
-    if (y_out) *y_out = oracle_round_bf16(exact);
+    if (y_out) {
+        uint16_t y = oracle_round_bf16(exact);
+        if ((flags & ORACLE_NO_NEG_ZERO) && y == 0x8000) y = 0;
+        *y_out = y;
+    }
 }
 
 typedef struct {
@@ -105,6 +129,7 @@ typedef struct {
     uint16_t *Y;
     double *ACC;
     int64_t M, N, K;
+    unsigned flags;
     int64_t begin, end;           /* flat element range [begin, end) over M*N */
 } job_t;
 
@@ -112,7 +137,7 @@ static void *run_job(void *arg) {
     job_t *j = (job_t *)arg;
     for (int64_t i = j->begin; i < j->end; ++i) {
         int64_t m = i / j->N, n = i % j->N;
-        one_element(j->X, j->W, j->R, j->N, j->K, m, n,
+        one_element(j->X, j->W, j->R, j->N, j->K, m, n, j->flags,
                     j->Y ? &j->Y[i] : NULL, j->ACC ? &j->ACC[i] : NULL);
     }
     return NULL;
@@ -126,10 +151,11 @@ static void *run_job(void *arg) {
  * result does not depend on the thread count. Returns 0, or -1 on bad
  * arguments / thread failure.
  */
-int oracle_addmm_bf16(const uint16_t *X, const uint16_t *W, const uint16_t *R,
-                      uint16_t *Y, double *ACC, int64_t M, int64_t N, int64_t K,
-                      int threads) {
+int oracle_addmm_bf16_ex(const uint16_t *X, const uint16_t *W, const uint16_t *R,
+                         uint16_t *Y, double *ACC, int64_t M, int64_t N, int64_t K,
+                         unsigned flags, int threads) {
     if (M < 0 || N < 0 || K < 0) return -1;
+    if (flags & ~(ORACLE_ROUND_PRODUCT | ORACLE_NO_NEG_ZERO)) return -1;
     int64_t total = M * N;
     if (total == 0) return 0;
     if (threads < 1) threads = 1;
@@ -139,7 +165,7 @@ int oracle_addmm_bf16(const uint16_t *X, const uint16_t *W, const uint16_t *R,
     int joined[256];
     job_t jobs[256];
     for (int t = 0; t < threads; ++t) {
-        jobs[t] = (job_t){X, W, R, Y, ACC, M, N, K, total * t / threads, total * (t + 1) / threads};
+        jobs[t] = (job_t){X, W, R, Y, ACC, M, N, K, flags, total * t / threads, total * (t + 1) / threads};
         joined[t] = 0;
         if (t == threads - 1 || pthread_create(&tid[t], NULL, run_job, &jobs[t]) != 0)
             run_job(&jobs[t]);    /* last range (or a failed spawn) runs here */
@@ -151,20 +177,35 @@ int oracle_addmm_bf16(const uint16_t *X, const uint16_t *W, const uint16_t *R,
     return 0;
 }
 
+/* The plain definition (one rounding, no sanitising). */
+int oracle_addmm_bf16(const uint16_t *X, const uint16_t *W, const uint16_t *R,
+                      uint16_t *Y, double *ACC, int64_t M, int64_t N, int64_t K,
+                      int threads) {
+    return oracle_addmm_bf16_ex(X, W, R, Y, ACC, M, N, K, 0u, threads);
+}
+
 /*
  * Selected elements only: for i < count, element (ms[i], ns[i]) is written to
  * Y[i] / ACC[i]. Used to check large problems at sampled positions.
- * Returns 0, or -1 if an index is out of range.
+ * Returns 0, or -1 if an index is out of range or a flag is unknown.
  */
+int oracle_addmm_bf16_points_ex(const uint16_t *X, const uint16_t *W, const uint16_t *R,
+                                int64_t M, int64_t N, int64_t K,
+                                const int64_t *ms, const int64_t *ns, int64_t count,
+                                unsigned flags, uint16_t *Y, double *ACC) {
+    if (flags & ~(ORACLE_ROUND_PRODUCT | ORACLE_NO_NEG_ZERO)) return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+        one_element(X, W, R, N, K, ms[i], ns[i], flags, Y ? &Y[i] : NULL, ACC ? &ACC[i] : NULL);
+    }
+    return 0;
+}
+
 int oracle_addmm_bf16_points(const uint16_t *X, const uint16_t *W, const uint16_t *R,
                              int64_t M, int64_t N, int64_t K,
                              const int64_t *ms, const int64_t *ns, int64_t count,
                              uint16_t *Y, double *ACC) {
-    for (int64_t i = 0; i < count; ++i) {
-        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
-        one_element(X, W, R, N, K, ms[i], ns[i], Y ? &Y[i] : NULL, ACC ? &ACC[i] : NULL);
-    }
-    return 0;
+    return oracle_addmm_bf16_points_ex(X, W, R, M, N, K, ms, ns, count, 0u, Y, ACC);
 }
 
 /* Elementwise rounding of a double array (for tests of the rounding step). */

@@ -13,7 +13,9 @@ What fixes the expected values (never the oracle itself):
   * brute force: exact Fraction sums on tiny shapes;
   * numpy's fp64 matmul (within its error bound) on a mid-sized problem;
   * exact invariants (permuting K, scaling X by a power of two);
-  * hand-derived single-element cases in tests/golden/closed_form_cases.txt.
+  * hand-derived single-element cases in tests/golden/closed_form_cases.txt, and for the
+    shard epilogue (two roundings, -0 written as +0) in tests/golden/shard_epilogue_cases.txt;
+  * integer rounding written out with Python integers (round half to even on 8 bits).
 """
 from __future__ import annotations
 
@@ -27,6 +29,8 @@ import torch
 from decode_skinny_addmm_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_form_cases.txt")
+GOLDEN_SHARD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "shard_epilogue_cases.txt")
+ROUND_PRODUCT, NO_NEG_ZERO = 1, 2   # the shard-epilogue flags of the oracle's *_ex entry points
 
 
 # ---------------------------------------------------------------- independent helpers
@@ -272,6 +276,61 @@ def pin_rows_independent(orc):
     assert changed[5] and changed.sum() == 1
 
 
+def rne_int_bf16(v: int) -> int:
+    """Nearest bf16 value to an integer |v| < 2^24 (as an int), ties to even: the integers
+    with 8 significant bits, written out with Python integer arithmetic."""
+    v = int(v)
+    a = abs(v)
+    if a < 256:
+        return v
+    q = 1 << (a.bit_length() - 8)      # spacing of bf16 values in [2^e, 2^(e+1))
+    n, rem = divmod(a, q)
+    if 2 * rem > q or (2 * rem == q and n % 2 == 1):
+        n += 1
+    return (n * q) if v > 0 else -(n * q)
+
+
+def pin_shard_golden_cases(orc):
+    """Hand-derived cases of the shard epilogue (tests/golden/shard_epilogue_cases.txt)."""
+    n_cases = 0
+    with open(GOLDEN_SHARD) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, flags, xs, ws, r, want = [p.strip() for p in line.split("|")]
+            x = np.array([float.fromhex(t) for t in xs.split()], dtype=np.float64)
+            w = np.array([float.fromhex(t) for t in ws.split()], dtype=np.float64)
+            K = x.shape[0]
+            X = _ub(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(1, K))
+            W = _ub(torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16).view(1, K))
+            R = _ub(torch.tensor([[float.fromhex(r)]], dtype=torch.float32).to(torch.bfloat16))
+            assert np.array_equal(_bits_to_f64(X)[0], x) and np.array_equal(_bits_to_f64(W)[0], w), name
+            Y, _ = orc.addmm_bf16(X, W, R, threads=1, flags=int(flags))
+            assert int(Y[0, 0]) == int(want, 16), "%s: got %04X want %s" % (name, Y[0, 0], want)
+            n_cases += 1
+    assert n_cases >= 10
+
+
+def pin_round_product_small_integers(orc):
+    """Integer inputs with the two-rounding epilogue: g = RNE(integer sum) and Y = RNE(g + r),
+    both rounded by integer arithmetic; the second value the oracle reports is g + r."""
+    M, N, K = 4, 37, 200
+    X, W, R = synth.small_int_inputs(M, N, K, seed=9)
+    X, W = X.abs(), W + 2              # x in {0, 1, 2}, w in {0, .., 4}: sums of ~500, exact
+    xi = X.to(torch.int64).numpy()
+    wi = W.to(torch.int64).numpy()
+    ri = R.to(torch.int64).numpy()
+    sums = xi @ wi.T
+    g = np.vectorize(rne_int_bf16)(sums)
+    want = np.vectorize(rne_int_bf16)(g + ri)
+    Y, ACC = orc.addmm_bf16(_ub(X), _ub(W), _ub(R), threads=2, flags=ROUND_PRODUCT)
+    assert np.array_equal(ACC, (g + ri).astype(np.float64))
+    assert np.array_equal(_bits_to_f64(Y), want.astype(np.float64))
+    # the case must separate two roundings from one
+    assert np.any(np.vectorize(rne_int_bf16)(sums + ri) != want)
+
+
 ALL_PINS = [
     pin_rounding_enumeration,
     pin_rounding_vs_torch,
@@ -284,4 +343,6 @@ ALL_PINS = [
     pin_permute_k,
     pin_scale_x,
     pin_rows_independent,
+    pin_shard_golden_cases,
+    pin_round_product_small_integers,
 ]

@@ -17,18 +17,25 @@ MUTANTS = {
     "transposed_W": ("W[n * K + k]", "W[k * N + n]"),
     "dropped_residual": ("k <= K", "k < K"),
     "dropped_first_product": ("for (int64_t k = 0; k <= K; ++k)", "for (int64_t k = 1; k <= K; ++k)"),
-    "residual_columns_reversed": ("R[m * N + n]", "R[m * N + (N - 1 - n)]"),
+    "residual_columns_reversed": (": bf16_bits_to_double(R[m * N + n]);", ": bf16_bits_to_double(R[m * N + (N - 1 - n)]);"),
     "X_reversed_in_k": ("X[m * K + k]", "X[m * K + (K - 1 - k)]"),
     "ties_away_from_zero": ("(fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0", "fl + 1.0"),
     "truncation": ("if (frac > 0.5) n = fl + 1.0;", "if (0) n = fl + 1.0;"),
     "nine_bit_mantissa": ("double q = ldexp(1.0, e - 7);", "double q = ldexp(1.0, e - 8);"),
-    "double_rounding_via_fp32": ("*y_out = oracle_round_bf16(exact);",
-                                 "*y_out = oracle_round_bf16((double)(float)exact);"),
+    "double_rounding_via_fp32": ("uint16_t y = oracle_round_bf16(exact);",
+                                 "uint16_t y = oracle_round_bf16((double)(float)exact);"),
     "no_compensation": ("double exact = s + c;", "double exact = s;"),
     "no_subnormal_clamp": ("if (e < -126) e = -126;", ""),
     "sign_dropped": ("return (uint16_t)(sign | ((u >> 16) & 0x7FFF));", "return (uint16_t)((u >> 16) & 0x7FFF);"),
     "fp32_accumulation": ("double t = s + p;", "double t = (double)(float)(s + p);"),
     "residual_scaled_twice": (": bf16_bits_to_double(R[m * N + n]);", ": 2.0 * bf16_bits_to_double(R[m * N + n]);"),
+    # the shard epilogue (flags)
+    "round_product_ignored": ("    if (round_product)\n        exact =", "    if (0)\n        exact ="),
+    "round_product_residual_twice": ("if (k == K && round_product) break;", "if (0) break;"),
+    "neg_zero_never_sanitised": ("if ((flags & ORACLE_NO_NEG_ZERO) && y == 0x8000) y = 0;", ""),
+    "neg_zero_always_sanitised": ("if ((flags & ORACLE_NO_NEG_ZERO) && y == 0x8000) y = 0;",
+                                  "if (y == 0x8000) y = 0;"),
+    "round_product_flag_swapped": ("(flags & ORACLE_ROUND_PRODUCT) != 0", "(flags & ORACLE_NO_NEG_ZERO) != 0"),
 }
 
 
