@@ -16,10 +16,13 @@ PATH_MFMA_LDS = 2
 PATH_GEMM = 3
 PATH_SIMT = 4
 PATH_GEMM_DMA = 5
+FLAG_ROUND_PRODUCT = 1  # shard epilogue: round the product sum to bf16, add R, round again
+FLAG_NO_NEG_ZERO = 2    # shard epilogue: write +0 for a -0 result
 CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
-            "skinny_addmm_bf16_acc_f32", "skinny_num_configs", "skinny_get_config",
+            "skinny_addmm_bf16_acc_f32", "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
+            "skinny_num_configs", "skinny_get_config",
             "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
             "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy")
 
@@ -69,6 +72,9 @@ def lib() -> ctypes.CDLL:
     L.skinny_addmm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     L.skinny_addmm_bf16_with_config.argtypes = [vp, vp, vp, vp, i64, i64, i64, cfgp, vp]
     L.skinny_addmm_bf16_acc_f32.argtypes = [vp, vp, vp, vp, i64, i64, i64, cfgp, vp]
+    L.skinny_addmm_bf16_shard.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_uint32, cfgp, vp]
+    L.skinny_addmm_bf16_shard_acc_f32.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_uint32,
+                                                  cfgp, vp]
     L.skinny_select_config.argtypes = [i64, i64, i64, cfgp]
     L.skinny_get_config.argtypes = [ctypes.c_int32, cfgp]
     L.skinny_config_resources.argtypes = [cfgp, ctypes.POINTER(SkinnyResources)]
@@ -81,6 +87,7 @@ def lib() -> ctypes.CDLL:
     for f in ("skinny_probe_null", "skinny_probe_read", "skinny_probe_copy"):
         getattr(L, f).restype = ctypes.c_int
     for f in ("skinny_addmm_bf16", "skinny_addmm_bf16_with_config", "skinny_addmm_bf16_acc_f32",
+              "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
               "skinny_select_config", "skinny_get_config", "skinny_config_resources",
               "skinny_num_configs", "skinny_last_hip_error"):
         getattr(L, f).restype = ctypes.c_int

@@ -83,18 +83,25 @@ skinny_config select(int64_t M, int64_t K) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-skinny_status run(const void *X, const void *W, const void *R, void *out, bool acc_out,
-                  int64_t M, int64_t N, int64_t K, const skinny_config *cfg, void *stream) {
+constexpr uint32_t kKnownFlags = SKINNY_FLAG_ROUND_PRODUCT | SKINNY_FLAG_NO_NEG_ZERO;
+
+skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void *out, int64_t ldo,
+                  bool acc_out, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                  const skinny_config *cfg, void *stream) {
     if (M < 0 || N < 0 || K < 0) return SKINNY_EINVAL;
+    if (flags & ~kKnownFlags) return SKINNY_EINVAL;
+    if (M > 1 && (ldr < N || ldo < N)) return SKINNY_EINVAL;
+    if (ldr < 0 || ldo < 0) return SKINNY_EINVAL;
     if (K % 8 != 0) return SKINNY_ENOTSUP;
     if (M == 0 || N == 0) return SKINNY_OK;
     if (!R || !out) return SKINNY_EINVAL;
+    if (!acc_out && out == R && ldo != ldr) return SKINNY_EINVAL;
     if (K > 0 && (!X || !W)) return SKINNY_EINVAL;
     if ((X && !aligned(X, 16)) || (W && !aligned(W, 16)) || !aligned(R, 2) ||
         !aligned(out, acc_out ? 4 : 2))
         return SKINNY_EALIGN;
     // kernel index arithmetic is 32-bit for sizes, 64-bit for offsets
-    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return SKINNY_ENOTSUP;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || ldr > INT_MAX || ldo > INT_MAX) return SKINNY_ENOTSUP;
     const skinny_config c = cfg ? *cfg : select(M, K);
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
@@ -112,7 +119,8 @@ skinny_status run(const void *X, const void *W, const void *R, void *out, bool a
     if ((M + mt - 1) / mt > 65535) return SKINNY_ENOTSUP;
     LaunchArgs a{static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(W),
                  static_cast<const uint16_t *>(R), out, M, N, K, acc_out,
-                 static_cast<hipStream_t>(stream)};
+                 static_cast<hipStream_t>(stream),
+                 Epilogue{(int)ldr, (int)ldo, acc_out ? (flags & SKINNY_FLAG_ROUND_PRODUCT) : flags}};
     const hipError_t err = e->launch(a);
     if (err != hipSuccess) {
         g_last_hip_error = (int32_t)err;
@@ -128,19 +136,32 @@ extern "C" {
 
 skinny_status skinny_addmm_bf16(const void *X, const void *W, const void *R, void *Y, int64_t M,
                                 int64_t N, int64_t K, void *stream) {
-    return skinny::run(X, W, R, Y, false, M, N, K, nullptr, stream);
+    return skinny::run(X, W, R, N, Y, N, false, M, N, K, 0, nullptr, stream);
 }
 
 skinny_status skinny_addmm_bf16_with_config(const void *X, const void *W, const void *R, void *Y,
                                             int64_t M, int64_t N, int64_t K,
                                             const skinny_config *cfg, void *stream) {
-    return skinny::run(X, W, R, Y, false, M, N, K, cfg, stream);
+    return skinny::run(X, W, R, N, Y, N, false, M, N, K, 0, cfg, stream);
 }
 
 skinny_status skinny_addmm_bf16_acc_f32(const void *X, const void *W, const void *R, float *ACC,
                                         int64_t M, int64_t N, int64_t K,
                                         const skinny_config *cfg, void *stream) {
-    return skinny::run(X, W, R, ACC, true, M, N, K, cfg, stream);
+    return skinny::run(X, W, R, N, ACC, N, true, M, N, K, 0, cfg, stream);
+}
+
+skinny_status skinny_addmm_bf16_shard(const void *X, const void *W, const void *R, int64_t ldr,
+                                      void *Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                      uint32_t flags, const skinny_config *cfg, void *stream) {
+    return skinny::run(X, W, R, ldr, Y, ldy, false, M, N, K, flags, cfg, stream);
+}
+
+skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const void *W, const void *R,
+                                              int64_t ldr, float *ACC, int64_t ldacc,
+                                              int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                              const skinny_config *cfg, void *stream) {
+    return skinny::run(X, W, R, ldr, ACC, ldacc, true, M, N, K, flags, cfg, stream);
 }
 
 skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out) {

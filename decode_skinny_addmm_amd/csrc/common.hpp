@@ -11,15 +11,23 @@ namespace skinny {
 
 // ----------------------------------------------------------------------------- launch plumbing
 
+// Epilogue layout and options, passed to every kernel by value: R[m, n] is R[m*ldr + n],
+// the output element (m, n) is out[m*ldy + n]; flags are SKINNY_FLAG_* bits.
+struct Epilogue {
+    int ldr, ldy;
+    uint32_t flags;
+};
+
 // Arguments of one call, already validated by the C ABI layer.
 struct LaunchArgs {
     const uint16_t *X;  // bf16 [M, K]
     const uint16_t *W;  // bf16 [N, K]
-    const uint16_t *R;  // bf16 [M, N]
-    void *out;          // bf16 [M, N] (Y) or float [M, N] (ACC)
+    const uint16_t *R;  // bf16 [M, N], row pitch ep.ldr
+    void *out;          // bf16 Y or float ACC [M, N], row pitch ep.ldy
     int64_t M, N, K;
     bool acc_out;       // true: write fp32 ACC instead of bf16 Y
     hipStream_t stream;
+    Epilogue ep;
 };
 
 // One compiled kernel instance: its public configuration, how to launch it, and the
@@ -58,6 +66,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// The one epilogue of every kernel: t is the fp32 sum of the K products for output (m, n),
+// r the residual already widened to fp32. Y = bf16(t + r), rounded once (RNE); with
+// SKINNY_FLAG_ROUND_PRODUCT the sum is first rounded to bf16 (the tensor-parallel shard
+// epilogue of the vLLM API page "fused_add_multicast_skinny_gemm": GEMM result in bf16, then
+// the residual added in fp32 and rounded again); with SKINNY_FLAG_NO_NEG_ZERO a -0 result is
+// written as +0 (that page keeps -0 free as its not-yet-written marker). The fp32 test output
+// (ACC) is the value that gets rounded.
+template <bool ACC>
+__device__ __forceinline__ void store_output(void *out, const Epilogue &ep, int m, int n, float t, float r) {
+    const float g = (ep.flags & SKINNY_FLAG_ROUND_PRODUCT) ? bf16_bits_to_f32(f32_to_bf16_rne(t)) : t;
+    const float y = g + r;
+    const size_t o = (size_t)m * ep.ldy + n;
+    if constexpr (ACC) {
+        static_cast<float *>(out)[o] = y;
+    } else {
+        uint16_t b = f32_to_bf16_rne(y);
+        if ((ep.flags & SKINNY_FLAG_NO_NEG_ZERO) && b == 0x8000u) b = 0;
+        static_cast<uint16_t *>(out)[o] = b;
+    }
 }
 
 // ---- cross-lane exchange steps (gfx950) ------------------------------------------------

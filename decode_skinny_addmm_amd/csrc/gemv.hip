@@ -33,7 +33,7 @@ template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL, bool A
 __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
-                                                       int M, int N, int K) {
+                                                       int M, int N, int K, Epilogue ep) {
     constexpr int V = RB * MT;                  // sums per lane per batch, index = m * RB + r
     constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
     constexpr int CF = V > 64 ? V / 64 : 1;     // sums per lane after the reduction
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
             const int idx = base + c;
             const int n = min(row_of(b * RB + idx % RB), N - 1);
             const int m = min(m0 + idx / RB, M - 1);
-            rres[q][c] = bf16_bits_to_f32(R[(size_t)m * N + n]);
+            rres[q][c] = bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]);
         }
     }
     if constexpr (TAIL) {
@@ -150,12 +150,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
                 float t = red[b][0][idx];
 #pragma unroll
                 for (int p = 1; p < KS; ++p) t += red[b][p][idx];
-                const size_t o = (size_t)m * N + n;
-                const float y = t + rres[q][c];
-                if constexpr (ACC)
-                    static_cast<float *>(out)[o] = y;
-                else
-                    static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+                store_output<ACC>(out, ep, m, n, t, rres[q][c]);
             }
         }
     }
@@ -165,10 +160,10 @@ template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL>
 void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
     if (a.acc_out)
         hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, true>), grid, block, 0, a.stream, a.X,
-                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
         hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, false>), grid, block, 0, a.stream, a.X,
-                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
 }
 
 template <int MT, int KS, int RB, int NB, int KV, bool CONTIG>

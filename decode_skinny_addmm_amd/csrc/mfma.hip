@@ -36,7 +36,7 @@ template <int KS, int T, int KU, int CT, bool ACC>
 __global__ __launch_bounds__(KS * 64) void mfma_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
-                                                       int M, int N, int K) {
+                                                       int M, int N, int K, Epilogue ep) {
     constexpr int NT = KS * 64;                 // threads
     constexpr int OUTS = T * CT * 256;          // D elements per workgroup (incl. padding)
     constexpr int PER_THREAD = (OUTS + NT - 1) / NT;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_kernel(const uint16_t *__restric
         const int t = tc / CT, c = tc % CT;
         const int m = min(m0 + 16 * c + (l & 15), M - 1);
         const int n = min((blockIdx.x + t * G) * 16 + 4 * (l >> 4) + r, N - 1);
-        rres[p] = bf16_bits_to_f32(R[(size_t)m * N + n]);
+        rres[p] = bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]);
     }
 
     // this wave's K slice, in 32-wide steps
@@ -139,12 +139,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_kernel(const uint16_t *__restric
         float sum = redf[e];
 #pragma unroll
         for (int g = 1; g < KS; ++g) sum += redf[g * OUTS + e];
-        const size_t o = (size_t)m * N + n;
-        const float y = sum + rres[p];
-        if constexpr (ACC)
-            static_cast<float *>(out)[o] = y;
-        else
-            static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+        store_output<ACC>(out, ep, m, n, sum, rres[p]);
     }
 }
 
@@ -154,10 +149,10 @@ hipError_t launch_mfma(const LaunchArgs &a) {
     dim3 block(KS * 64);
     if (a.acc_out)
         hipLaunchKernelGGL((mfma_kernel<KS, T, KU, CT, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
-                           a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
         hipLaunchKernelGGL((mfma_kernel<KS, T, KU, CT, false>), grid, block, 0, a.stream, a.X, a.W, a.R,
-                           a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     return hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ template <int BN, int BM, int NS, bool ACC>
 __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
-                                                       int M, int N, int K, int n_tiles, int m_tiles) {
+                                                       int M, int N, int K, int n_tiles, int m_tiles, Epilogue ep) {
     constexpr int WN = BN / 2, WM = BM / 2;          // wave block
     constexpr int TN = WN / 16, TM = WM / 16;        // MFMA tiles per wave
     static_assert(TN >= 1 && TM >= 1, "tile too small");
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid + 256 * i;
-        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * N + min(n0 + e % BN, N - 1)];
+        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * ep.ldr + min(n0 + e % BN, N - 1)];
     }
 
     f32x4_t acc[TN][TM];
@@ -199,12 +199,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
-            const size_t o = (size_t)m * N + n;
-            const float y = C[nl * (BM + 4) + ml] + bf16_bits_to_f32(rv[i]);
-            if constexpr (ACC)
-                static_cast<float *>(out)[o] = y;
-            else
-                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+            store_output<ACC>(out, ep, m, n, C[nl * (BM + 4) + ml], bf16_bits_to_f32(rv[i]));
         }
     }
 }
@@ -218,10 +213,10 @@ hipError_t launch_dma(const LaunchArgs &a) {
     dim3 block(256);
     if (a.acc_out)
         hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     else
         hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ template <int BN, int BM, int D, int KG, bool ACC>
 __global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__restrict__ X,
                                                         const uint16_t *__restrict__ W,
                                                         const uint16_t *R, void *out,
-                                                        int M, int N, int K, int n_tiles, int m_tiles) {
+                                                        int M, int N, int K, int n_tiles, int m_tiles, Epilogue ep) {
     constexpr int WN = BN / 2, WM = BM / 2;          // wave block
     constexpr int TN = WN / 16, TM = WM / 16;        // MFMA tiles per wave
     constexpr int LW = BN * 16 / 256;                // 16-byte W loads per thread per stage
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__r
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = threadIdx.x + 256 * KG * i;
-        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * N + min(n0 + e % BN, N - 1)];
+        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * ep.ldr + min(n0 + e % BN, N - 1)];
     }
 
     f32x4_t acc[TN][TM];
@@ -201,12 +201,7 @@ __global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(const uint16_t *__r
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
-            const size_t o = (size_t)m * N + n;
-            const float y = C[nl * (BM + 4) + ml] + bf16_bits_to_f32(rv[i]);
-            if constexpr (ACC)
-                static_cast<float *>(out)[o] = y;
-            else
-                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+            store_output<ACC>(out, ep, m, n, C[nl * (BM + 4) + ml], bf16_bits_to_f32(rv[i]));
         }
     }
 }
@@ -220,10 +215,10 @@ hipError_t launch_gemm(const LaunchArgs &a) {
     dim3 block(256 * KG);
     if (a.acc_out)
         hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, KG, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     else
         hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM, D, KG, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles);
+                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     return hipGetLastError();
 }
 

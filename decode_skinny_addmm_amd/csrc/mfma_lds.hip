@@ -41,7 +41,7 @@ template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL, bool 
 __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__restrict__ X,
                                                            const uint16_t *__restrict__ W,
                                                            const uint16_t *R, void *out,
-                                                           int M, int N, int K) {
+                                                           int M, int N, int K, Epilogue ep) {
     static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8 || RB == 16, "RB must divide 16");
     constexpr int NT = KS * 64;
     constexpr int OUTS = NB * RB * 16 * CT;       // outputs per workgroup (incl. padded m)
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
         const int br = e % (RB * NB);  // batch * RB + row
         const int m = min(m0 + e / (RB * NB), M - 1);
         const int n = min(row_of(br), N - 1);
-        rres[p] = bf16_bits_to_f32(R[(size_t)m * N + n]);
+        rres[p] = bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]);
     }
     if constexpr (TAIL) {
 #pragma unroll
@@ -180,12 +180,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
         float t = 0.0f;
 #pragma unroll
         for (int q = 0; q < KS; ++q) t += redf[(b * KS + q) * CT * LV * 4 + idx];
-        const size_t o = (size_t)m * N + n;
-        const float y = t + rres[p];
-        if constexpr (ACC)
-            static_cast<float *>(out)[o] = y;
-        else
-            static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+        store_output<ACC>(out, ep, m, n, t, rres[p]);
     }
 }
 
@@ -193,10 +188,10 @@ template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL>
 void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
     if (a.acc_out)
         hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, true>), grid, block, 0, a.stream,
-                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
         hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, false>), grid, block, 0, a.stream,
-                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
 }
 
 template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL>

@@ -24,7 +24,8 @@ template <> struct Vec<4> { typedef uint32_t type __attribute__((ext_vector_type
 // KU: vectors per row in flight per step; VW: bf16 per vector.
 template <int MT, int BS, int OPB, int KU, int VW, bool ACC>
 __global__ __launch_bounds__(BS) void simt_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
-                                                  const uint16_t *R, void *out, int M, int N, int K) {
+                                                  const uint16_t *R, void *out, int M, int N, int K,
+                                                  Epilogue ep) {
     using vec = typename Vec<VW>::type;
     constexpr int DW = VW / 2;                   // dwords per vector
     constexpr int WAVES = BS / 64;
@@ -93,12 +94,7 @@ __global__ __launch_bounds__(BS) void simt_kernel(const uint16_t *__restrict__ X
             float t = red[0][idx];
 #pragma unroll
             for (int q = 1; q < WAVES; ++q) t += red[q][idx];
-            const size_t o = (size_t)m * N + n;
-            const float y = t + bf16_bits_to_f32(R[o]);
-            if constexpr (ACC)
-                static_cast<float *>(out)[o] = y;
-            else
-                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(y);
+            store_output<ACC>(out, ep, m, n, t, bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]));
         }
     }
 }
@@ -109,10 +105,10 @@ hipError_t launch_simt(const LaunchArgs &a) {
     dim3 block(BS);
     if (a.acc_out)
         hipLaunchKernelGGL((simt_kernel<MT, BS, OPB, KU, VW, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
-                           a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
         hipLaunchKernelGGL((simt_kernel<MT, BS, OPB, KU, VW, false>), grid, block, 0, a.stream, a.X, a.W, a.R,
-                           a.out, (int)a.M, (int)a.N, (int)a.K);
+                           a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ import ctypes
 
 import torch
 
-from ._lib import CONFIG_FIELDS, SkinnyConfig, SkinnyError, SkinnyResources, check, lib  # noqa: F401
+from ._lib import (CONFIG_FIELDS, FLAG_NO_NEG_ZERO, FLAG_ROUND_PRODUCT, SkinnyConfig, SkinnyError,  # noqa: F401
+                   SkinnyResources, check, lib)
 
 
 def _as_config(cfg) -> SkinnyConfig | None:
@@ -94,6 +95,78 @@ def addmm_acc_f32(X, W, R, out: torch.Tensor | None = None, config=None, stream=
                                              M, N, K, ctypes.byref(c) if c is not None else None,
                                              _stream_ptr(stream, X.device))
     check(st, "skinny_addmm_bf16_acc_f32")
+    return out
+
+
+def _check_shard_operands(X, W, R, out, out_dtype):
+    """Like _check_operands, but R and out may be row-major views into wider matrices: each
+    needs unit column stride and a row stride >= N (the leading dimension passed on)."""
+    for name, t in (("X", X), ("W", W), ("R", R), ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if t.dim() != 2:
+            raise ValueError("%s must be 2-D" % name)
+    for name, t in (("X", X), ("W", W)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (row-major)" % name)
+    for name, t in (("X", X), ("W", W), ("R", R)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16" % name)
+    if out.dtype != out_dtype:
+        raise ValueError("out must be %s" % out_dtype)
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K] with K = X.shape[1]")
+    if tuple(R.shape) != (M, N) or tuple(out.shape) != (M, N):
+        raise ValueError("R and out must be [M, N] = [%d, %d]" % (M, N))
+    for name, t in (("R", R), ("out", out)):
+        if N > 1 and t.stride(1) != 1:
+            raise ValueError("%s must have unit column stride" % name)
+        if M > 1 and t.stride(0) < N:
+            raise ValueError("%s row stride must be >= N" % name)
+    if len({t.device for t in (X, W, R, out)}) != 1:
+        raise ValueError("all operands must be on the same device")
+    return M, N, K, (R.stride(0) if M > 1 else N), (out.stride(0) if M > 1 else N)
+
+
+def _shard_flags(round_product: bool, no_neg_zero: bool) -> int:
+    return (FLAG_ROUND_PRODUCT if round_product else 0) | (FLAG_NO_NEG_ZERO if no_neg_zero else 0)
+
+
+def addmm_shard(X, W, R, out=None, round_product=False, no_neg_zero=False, config=None,
+                stream=None) -> torch.Tensor:
+    """Tensor-parallel shard form via skinny_addmm_bf16_shard: R and out may be column blocks
+    of wider row-major matrices (their row strides are passed as leading dimensions).
+    round_product: round the product sum to bf16 before adding R (two roundings);
+    no_neg_zero: write +0 for a -0 result."""
+    if out is None:
+        out = torch.empty(R.shape, dtype=torch.bfloat16, device=R.device)
+    M, N, K, ldr, ldy = _check_shard_operands(X, W, R, out, torch.bfloat16)
+    c = _as_config(config)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_addmm_bf16_shard(X.data_ptr(), W.data_ptr(), R.data_ptr(), ldr, out.data_ptr(), ldy,
+                                           M, N, K, _shard_flags(round_product, no_neg_zero),
+                                           ctypes.byref(c) if c is not None else None,
+                                           _stream_ptr(stream, X.device))
+    check(st, "skinny_addmm_bf16_shard")
+    return out
+
+
+def addmm_shard_acc_f32(X, W, R, out=None, round_product=False, config=None, stream=None) -> torch.Tensor:
+    """Test entry of the shard form: the fp32 value each output is rounded from."""
+    if out is None:
+        out = torch.empty(R.shape, dtype=torch.float32, device=R.device)
+    M, N, K, ldr, lda = _check_shard_operands(X, W, R, out, torch.float32)
+    c = _as_config(config)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_addmm_bf16_shard_acc_f32(X.data_ptr(), W.data_ptr(), R.data_ptr(), ldr, out.data_ptr(),
+                                                   lda, M, N, K, _shard_flags(round_product, False),
+                                                   ctypes.byref(c) if c is not None else None,
+                                                   _stream_ptr(stream, X.device))
+    check(st, "skinny_addmm_bf16_shard_acc_f32")
     return out
 
 

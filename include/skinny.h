@@ -133,6 +133,42 @@ SKINNY_API skinny_status skinny_addmm_bf16_acc_f32(const void *X, const void *W,
                                         int64_t M, int64_t N, int64_t K,
                                         const skinny_config *cfg, void *stream);
 
+/*
+ * Tensor-parallel shard form (the vLLM API page "fused_add_multicast_skinny_gemm": each rank
+ * multiplies its N/g rows of W and writes its columns of a wider output, with R taken from the
+ * same wide layout):
+ *
+ *     Y[m*ldy + n] = bf16( sum_k X[m, k] * W[n, k]  +  R[m*ldr + n] ),  0 <= n < N
+ *
+ * R and Y are row-major with row pitches ldr and ldy (elements, each >= N when M > 1); Y and
+ * R may point at a column offset inside a wider matrix, and elements outside the M x N block
+ * are neither read nor written. `flags` is a bit set of SKINNY_FLAG_*:
+ *   SKINNY_FLAG_ROUND_PRODUCT  round the fp32 sum of products to bf16 first, then add R in
+ *                              fp32 and round again (that page's epilogue; two roundings);
+ *   SKINNY_FLAG_NO_NEG_ZERO    write +0 wherever the bf16 result is -0 (that page reserves -0
+ *                              as its not-yet-written marker).
+ * Unknown flag bits give SKINNY_EINVAL. Y may be exactly R only with ldy == ldr (else
+ * SKINNY_EINVAL). cfg NULL = the selected configuration. Everything else as
+ * skinny_addmm_bf16_with_config.
+ */
+enum {
+    SKINNY_FLAG_ROUND_PRODUCT = 1u,
+    SKINNY_FLAG_NO_NEG_ZERO = 2u
+};
+SKINNY_API skinny_status skinny_addmm_bf16_shard(const void *X, const void *W, const void *R, int64_t ldr,
+                                                 void *Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                 uint32_t flags, const skinny_config *cfg, void *stream);
+
+/*
+ * Test entry of the shard form: the fp32 value each output would be rounded from (with
+ * SKINNY_FLAG_ROUND_PRODUCT: bf16(sum) + R), written to ACC (float, row pitch ldacc).
+ * SKINNY_FLAG_NO_NEG_ZERO acts on bf16 results only and is accepted and ignored here.
+ */
+SKINNY_API skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const void *W, const void *R,
+                                                         int64_t ldr, float *ACC, int64_t ldacc,
+                                                         int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                                         const skinny_config *cfg, void *stream);
+
 /* Number of configurations built into the library, and the i-th of them (0-based). */
 SKINNY_API int32_t skinny_num_configs(void);
 SKINNY_API skinny_status skinny_get_config(int32_t index, skinny_config *out);

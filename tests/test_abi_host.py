@@ -131,3 +131,19 @@ def test_acc_needs_4_byte_alignment(L):
 def test_config_checks(L, cfg, expect):
     c = _lib.SkinnyConfig(*cfg)
     assert L.skinny_addmm_bf16_with_config(A16, A16, A16, A16, 1, 8, 8, ctypes.byref(c), None) == expect
+
+
+@pytest.mark.parametrize("ldr,ldy,M,flags,out_is_r,expect", [
+    (7, 8, 2, 0, False, 1),          # R pitch below N
+    (8, 7, 2, 0, False, 1),          # Y pitch below N
+    (-8, 8, 1, 0, False, 1),         # negative pitch
+    (8, 8, 2, 4, False, 1),          # unknown flag bit
+    (8, 16, 2, 0, True, 1),          # Y is R with another pitch
+    (8, 8, 0, 3, False, 0),          # M == 0: no-op, flags known
+])
+def test_shard_argument_checks(L, ldr, ldy, M, flags, out_is_r, expect):
+    Y = A16 if out_is_r else A16 + 0x1000
+    assert L.skinny_addmm_bf16_shard(A16, A16, A16, ldr, Y, ldy, M, 8, 8, flags, None, None) == expect
+    if not out_is_r:  # the fp32 test output never aliases R
+        assert L.skinny_addmm_bf16_shard_acc_f32(A16, A16, A16, ldr, A16 + 0x1000, ldy, M, 8, 8, flags,
+                                                 None, None) == expect
