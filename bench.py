@@ -17,6 +17,10 @@ oracle timed on this host as a baseline.
 Other modes write JSONL rows (one per configuration or M) to --out:
   --mode sweep    every built configuration at --m (default 16)
   --mode mcurve   M in {1,2,4,8,16,32,64,128,256}, library-selected configuration
+  --mode shard    the tensor-parallel shard form (vLLM API page "fused_add_multicast_skinny_gemm"):
+                  N = 7168/--shards columns for rank --rank, R and Y as column blocks of the
+                  full-width matrices, two roundings and no -0, W rotated over >= 40 copies
+  --mode shard-sweep   the same over every built configuration
 """
 from __future__ import annotations
 
@@ -124,6 +128,34 @@ class Workload:
         torch.cuda.synchronize()
         log("inputs M=%d copies=%d ready in %.1fs (%.1f MB of W+R)" % (
             M, copies, time.time() - t0, copies * (N * K + M * N) * 2 / 1e6))
+
+
+class ShardWorkload:
+    """One rank's share of the N-sharded op: W holds N_total/shards rows (C seeded copies, enough
+    to stream from HBM), R and Y are column blocks of [M, N_total] matrices at the rank's offset."""
+
+    def __init__(self, M: int, copies: int, shards: int, rank: int, N_total: int = N_DIM, K: int = K_DIM):
+        import torch
+
+        from decode_skinny_addmm_amd import synth
+        t0 = time.time()
+        N = N_total // shards
+        c0 = rank * N
+        X, ws, rs = synth.make_inputs(M, N, K, copies=copies)
+        self.host = (X, ws[0], rs[0])
+        self.M, self.N, self.K, self.copies, self.N_total, self.c0 = M, N, K, copies, N_total, c0
+        self.X = X.cuda()
+        self.W = [w.cuda() for w in ws]
+        self.Rwide = [torch.zeros((M, N_total), dtype=torch.bfloat16, device="cuda") for _ in rs]
+        for rw, r in zip(self.Rwide, rs):
+            rw[:, c0:c0 + N].copy_(r.cuda())
+        self.Ywide = [torch.zeros((M, N_total), dtype=torch.bfloat16, device="cuda") for _ in rs]
+        self.R = [rw[:, c0:c0 + N] for rw in self.Rwide]
+        self.Y = [yw[:, c0:c0 + N] for yw in self.Ywide]
+        del ws, rs
+        torch.cuda.synchronize()
+        log("shard inputs M=%d N=%d (rank %d of %d) copies=%d ready in %.1fs (%.1f MB of W)" % (
+            M, N, rank, shards, copies, time.time() - t0, copies * N * K * 2 / 1e6))
 
 
 def time_graph(launch, wl, calls: int, warmup: int, steps: int):
@@ -428,6 +460,67 @@ def sweep_rows(args, sk, Ms, config_lists):
         out.close()
 
 
+def run_shard(args, sk):
+    """The tensor-parallel shard form: N = 7168/shards columns per rank, W rotated over enough
+    copies to exceed L2 and the Infinity Cache, R read from and Y written into column blocks of
+    the full-width matrices, both shard-epilogue flags on (two roundings, no -0)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from decode_skinny_addmm_amd import synth
+    Ms = [int(x) for x in args.ms.split(",")] if args.ms else [1, 2, 4, 8]
+    N = N_DIM // args.shards
+    copies = args.copies if args.copies != 6 else max(40, -(-308_000_000 // (N * K_DIM * 2)))
+    configs = None
+    if args.paths:
+        paths = {int(x) for x in args.paths.split(",")}
+    out = open(args.out, "a") if args.out else None
+    for M in Ms:
+        wl = ShardWorkload(M, copies, args.shards, args.rank)
+        if args.mode == "shard-sweep":
+            configs = [c for c in sk.configs() if -(-M // c["m_tile"]) <= 2 and (not args.paths or c["path"] in paths)]
+        for cfg in (configs or [args.config or sk.select_config(M, N)]):
+            def launch(X, W, R, Y, cfg=cfg):
+                return sk.addmm_shard(X, W, R, out=Y, round_product=True, no_neg_zero=True, config=cfg)
+            row = {"mode": "shard", "m": M, "n": N, "k": K_DIM, "n_total": N_DIM, "shards": args.shards,
+                   "rank": args.rank, "copies": copies, "calls": args.calls, "config": cfg}
+            try:
+                per, total_ms = time_graph(launch, wl, args.calls, args.warmup, args.steps)
+                us = [p / args.calls for p in per]
+                mean_us = total_ms * 1000.0 / (args.steps * args.calls)
+                nbytes = algorithmic_bytes(M, N, K_DIM)
+                row.update(summarize(us))
+                row.update({"mean_us_total": mean_us, "gbs": nbytes / (mean_us * 1e-6) / 1e9,
+                            "frac_hbm": nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                            "bytes_per_launch": nbytes})
+                # sampled parity against the oracle with the same flags (two roundings: the result
+                # can sit one bf16 step of the rounded product away from the oracle's)
+                X, W, R = wl.host
+                Y = torch.zeros_like(wl.Rwide[0])
+                Yv = Y[:, wl.c0:wl.c0 + N]
+                launch(wl.X, wl.W[0], wl.R[0], Yv)
+                torch.cuda.synchronize()
+                rng = np.random.default_rng(0)
+                ms = rng.integers(0, M, 256)
+                ns = rng.integers(0, N, 256)
+                yo, _ = oracle.addmm_bf16_points(synth.bits(X), synth.bits(W), synth.bits(R), ms, ns,
+                                                 flags=oracle.ROUND_PRODUCT | oracle.NO_NEG_ZERO)
+                yg = synth.bits(Yv.contiguous())[ms, ns]
+                row["matches_oracle_frac"] = float(np.mean(yg == yo))
+            except Exception as e:  # noqa: BLE001
+                row.update({"valid": False, "error": "%s: %s" % (type(e).__name__, e)})
+            line = json.dumps(row, sort_keys=True)
+            print(line, flush=True)
+            if out:
+                out.write(line + "\n")
+                out.flush()
+        del wl
+        torch.cuda.empty_cache()
+    if out:
+        out.close()
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -437,7 +530,10 @@ def main():
     p.add_argument("--copies", type=int, default=6)
     p.add_argument("--calls", type=int, default=500, help="launches captured per graph (one step)")
     p.add_argument("--config", type=parse_config, default=None)
-    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib"), default="default")
+    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib", "shard", "shard-sweep"),
+                   default="default")
+    p.add_argument("--shards", type=int, default=8, help="shard/shard-sweep: ranks the 7168 columns split over")
+    p.add_argument("--rank", type=int, default=3, help="shard/shard-sweep: which rank's column block")
     p.add_argument("--out", type=str, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -466,6 +562,8 @@ def main():
         run_probe(args, sk)
     elif args.mode == "calib":
         run_calib(args, sk)
+    elif args.mode in ("shard", "shard-sweep"):
+        run_shard(args, sk)
     elif args.mode == "sweep":
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
         paths = {int(x) for x in args.paths.split(",")} if args.paths else None

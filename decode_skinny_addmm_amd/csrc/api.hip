@@ -64,18 +64,22 @@ const KernelEntry *find_entry(const skinny_config &c, int64_t M) {
     return best;
 }
 
-skinny_config table_row(int64_t M) {
+skinny_config table_row(int64_t M, int64_t N) {
+    const int nn = (int)(sizeof(kTableNarrow) / sizeof(kTableNarrow[0]));
+    if (N <= kNarrowN && M <= kTableNarrow[nn - 1].max_m)
+        for (int i = 0; i < nn; ++i)
+            if (M <= kTableNarrow[i].max_m) return kTableNarrow[i].cfg;
     const int n = (int)(sizeof(kTable) / sizeof(kTable[0]));
     for (int i = 0; i < n; ++i)
         if (M <= kTable[i].max_m) return kTable[i].cfg;
     return kTable[n - 1].cfg;
 }
 
-// The table's choice for M, unless that kernel cannot take this K (GEMV instances hold
+// The table's choice for (M, N), unless that kernel cannot take this K (GEMV instances hold
 // their K slice in registers; the direct-to-LDS GEMM needs whole 128-wide K stages); then
 // the general configuration for that M range, which takes any K.
-skinny_config select(int64_t M, int64_t K) {
-    const skinny_config c = table_row(M);
+skinny_config select(int64_t M, int64_t N, int64_t K) {
+    const skinny_config c = table_row(M, N);
     const KernelEntry *e = find_entry(c, M);
     if (e && K <= e->max_k() && K % e->k_align == 0) return c;
     return M <= 16 ? kFallbackSmall : kFallbackLarge;
@@ -102,7 +106,7 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
         return SKINNY_EALIGN;
     // kernel index arithmetic is 32-bit for sizes, 64-bit for offsets
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX || ldr > INT_MAX || ldo > INT_MAX) return SKINNY_ENOTSUP;
-    const skinny_config c = cfg ? *cfg : select(M, K);
+    const skinny_config c = cfg ? *cfg : select(M, N, K);
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
         c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0)
@@ -166,7 +170,7 @@ skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const void *W, cons
 
 skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out) {
     if (!out || M < 0 || N < 0 || K < 0) return SKINNY_EINVAL;
-    *out = skinny::select(M, K);
+    *out = skinny::select(M, N, K);
     return SKINNY_OK;
 }
 

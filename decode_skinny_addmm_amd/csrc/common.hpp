@@ -30,6 +30,14 @@ struct LaunchArgs {
     Epilogue ep;
 };
 
+// True for the plain [M, N] output with no shard flags. The kernels on the tuned path have an
+// instantiation for that case (GEN = false) whose epilogue takes the pitches from N and has
+// no flag tests; the general instantiation (GEN = true) serves the shard form and the fp32
+// test output. The sum of products is the same code in both.
+inline bool plain_epilogue(const LaunchArgs &a) {
+    return a.ep.flags == 0 && a.ep.ldr == a.N && a.ep.ldy == a.N;
+}
+
 // One compiled kernel instance: its public configuration, how to launch it, and the
 // address of its device function (for attribute queries).
 struct KernelEntry {

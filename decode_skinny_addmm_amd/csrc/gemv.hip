@@ -29,11 +29,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // MT: rows of X per pass; KS: waves (K split); RB: rows per batch; NB: batches per
 // workgroup; KV: 16-byte vectors per lane per row (K <= KV * KS * 512).
-template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL, bool ACC>
+template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL, bool ACC, bool GEN>
 __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
                                                        int M, int N, int K, Epilogue ep) {
+    const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
     constexpr int V = RB * MT;                  // sums per lane per batch, index = m * RB + r
     constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
     constexpr int CF = V > 64 ? V / 64 : 1;     // sums per lane after the reduction
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
             const int idx = base + c;
             const int n = min(row_of(b * RB + idx % RB), N - 1);
             const int m = min(m0 + idx / RB, M - 1);
-            rres[q][c] = bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]);
+            rres[q][c] = bf16_bits_to_f32(R[(size_t)m * epi.ldr + n]);
         }
     }
     if constexpr (TAIL) {
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
                 float t = red[b][0][idx];
 #pragma unroll
                 for (int p = 1; p < KS; ++p) t += red[b][p][idx];
-                store_output<ACC>(out, ep, m, n, t, rres[q][c]);
+                store_output<ACC>(out, epi, m, n, t, rres[q][c]);
             }
         }
     }
@@ -159,11 +160,14 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
 template <int MT, int KS, int RB, int NB, int KV, bool CONTIG, bool TAIL>
 void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
     if (a.acc_out)
-        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, true>), grid, block, 0, a.stream, a.X,
-                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, true, true>), grid, block, 0, a.stream,
+                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+    else if (plain_epilogue(a))
+        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, false, false>), grid, block, 0, a.stream,
+                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
-        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, false>), grid, block, 0, a.stream, a.X,
-                           a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+        hipLaunchKernelGGL((gemv_kernel<MT, KS, RB, NB, KV, CONTIG, TAIL, false, true>), grid, block, 0, a.stream,
+                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
 }
 
 template <int MT, int KS, int RB, int NB, int KV, bool CONTIG>
@@ -188,8 +192,8 @@ int64_t gemv_max_k() { return (int64_t)KV * KS * 64 * 8; }
     KernelEntry {                                                                                  \
         skinny_config{SKINNY_PATH_GEMV, 64 * KS, RB * NB, KV, CONTIG ? 9 : 8, MT, KS},             \
             &launch_gemv<MT, KS, RB, NB, KV, CONTIG>,                                              \
-            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, false>,                  \
-            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, true>, &gemv_max_k<KS, KV> \
+            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, false, false>,           \
+            (const void *)&gemv_kernel<MT, KS, RB, NB, KV, CONTIG, false, true, true>, &gemv_max_k<KS, KV> \
     }
 
 #include "gemv_instances.inc"

@@ -64,11 +64,12 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // BN: rows of W per workgroup; BM: rows of X per workgroup; NS: LDS stages in the ring.
-template <int BN, int BM, int NS, bool ACC>
+template <int BN, int BM, int NS, bool ACC, bool GEN>
 __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
                                                        int M, int N, int K, int n_tiles, int m_tiles, Epilogue ep) {
+    const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
     constexpr int WN = BN / 2, WM = BM / 2;          // wave block
     constexpr int TN = WN / 16, TM = WM / 16;        // MFMA tiles per wave
     static_assert(TN >= 1 && TM >= 1, "tile too small");
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid + 256 * i;
-        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * ep.ldr + min(n0 + e % BN, N - 1)];
+        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * epi.ldr + min(n0 + e % BN, N - 1)];
     }
 
     f32x4_t acc[TN][TM];
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
-            store_output<ACC>(out, ep, m, n, C[nl * (BM + 4) + ml], bf16_bits_to_f32(rv[i]));
+            store_output<ACC>(out, epi, m, n, C[nl * (BM + 4) + ml], bf16_bits_to_f32(rv[i]));
         }
     }
 }
@@ -212,11 +213,14 @@ hipError_t launch_dma(const LaunchArgs &a) {
     dim3 grid((unsigned)(groups * 8 * m_tiles));
     dim3 block(256);
     if (a.acc_out)
-        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, true>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, true, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
+                           a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
+    else if (plain_epilogue(a))
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false, false>), grid, block, 0, a.stream, a.X, a.W, a.R,
+                           a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     else
-        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false>), grid, block, 0, a.stream, a.X, a.W, a.R, a.out,
-                           (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
+                           a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     return hipGetLastError();
 }
 
@@ -227,8 +231,8 @@ int64_t dma_max_k() { return INT64_MAX; }
 #define DMA_ENTRY(BN, BM, NS)                                                                      \
     KernelEntry {                                                                                  \
         skinny_config{SKINNY_PATH_GEMM_DMA, 256, BN, NS, 8, BM, 1}, &launch_dma<BN, BM, NS>,       \
-            (const void *)&mfma_dma_kernel<BN, BM, NS, false>,                                     \
-            (const void *)&mfma_dma_kernel<BN, BM, NS, true>, &dma_max_k, kKC                      \
+            (const void *)&mfma_dma_kernel<BN, BM, NS, false, false>,                              \
+            (const void *)&mfma_dma_kernel<BN, BM, NS, true, true>, &dma_max_k, kKC                \
     }
 
 const KernelEntry kDmaEntries[] = {

@@ -37,11 +37,12 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 // XL: the rows of X (those < M) are loaded first, in contiguous 1 KB pieces, and turned into
 // fragments through the staging slice; otherwise the fragments are loaded in fragment order
 // (16 rows x 64 B per instruction) after the W batches.
-template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL, bool ACC>
+template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL, bool ACC, bool GEN>
 __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__restrict__ X,
                                                            const uint16_t *__restrict__ W,
                                                            const uint16_t *R, void *out,
                                                            int M, int N, int K, Epilogue ep) {
+    const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
     static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8 || RB == 16, "RB must divide 16");
     constexpr int NT = KS * 64;
     constexpr int OUTS = NB * RB * 16 * CT;       // outputs per workgroup (incl. padded m)
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
         const int br = e % (RB * NB);  // batch * RB + row
         const int m = min(m0 + e / (RB * NB), M - 1);
         const int n = min(row_of(br), N - 1);
-        rres[p] = bf16_bits_to_f32(R[(size_t)m * ep.ldr + n]);
+        rres[p] = bf16_bits_to_f32(R[(size_t)m * epi.ldr + n]);
     }
     if constexpr (TAIL) {
 #pragma unroll
@@ -180,18 +181,21 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
         float t = 0.0f;
 #pragma unroll
         for (int q = 0; q < KS; ++q) t += redf[(b * KS + q) * CT * LV * 4 + idx];
-        store_output<ACC>(out, ep, m, n, t, rres[p]);
+        store_output<ACC>(out, epi, m, n, t, rres[p]);
     }
 }
 
 template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL, bool TAIL>
 void launch_one(const LaunchArgs &a, dim3 grid, dim3 block) {
     if (a.acc_out)
-        hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, true>), grid, block, 0, a.stream,
-                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+        hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, true, true>), grid, block, 0,
+                           a.stream, a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+    else if (plain_epilogue(a))
+        hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, false, false>), grid, block, 0,
+                           a.stream, a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
     else
-        hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, false>), grid, block, 0, a.stream,
-                           a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
+        hipLaunchKernelGGL((mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, TAIL, false, true>), grid, block, 0,
+                           a.stream, a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, a.ep);
 }
 
 template <int KS, int RB, int NB, int CT, bool CONTIG, bool XL>
@@ -219,8 +223,8 @@ int64_t lds_max_k() { return (int64_t)KS * 512; }
         skinny_config{SKINNY_PATH_MFMA_LDS, 64 * KS, RB * NB, RB, XL ? 10 : (CONTIG ? 9 : 8),     \
                       16 * CT, KS},                                                                \
             &launch_mfma_lds<KS, RB, NB, CT, CONTIG, XL>,                                          \
-            (const void *)&mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, false, false>,              \
-            (const void *)&mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, false, true>, &lds_max_k<KS> \
+            (const void *)&mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, false, false, false>,       \
+            (const void *)&mfma_lds_kernel<KS, RB, NB, CT, CONTIG, XL, false, true, true>, &lds_max_k<KS> \
     }
 
 const KernelEntry kMfmaLdsEntries[] = {
