@@ -479,7 +479,7 @@ def run_shard(args, sk):
     for M in Ms:
         wl = ShardWorkload(M, copies, args.shards, args.rank)
         if args.mode == "shard-sweep":
-            configs = [c for c in sk.configs() if -(-M // c["m_tile"]) <= 2 and (not args.paths or c["path"] in paths)]
+            configs = [c for c in sk.configs() if -(-M // c["m_tile"]) <= 4 and (not args.paths or c["path"] in paths)]
         for cfg in (configs or [args.config or sk.select_config(M, N)]):
             def launch(X, W, R, Y, cfg=cfg):
                 return sk.addmm_shard(X, W, R, out=Y, round_product=True, no_neg_zero=True, config=cfg)
