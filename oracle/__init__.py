@@ -23,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_KBIT_SRC = os.path.join(_HERE, "kbit.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _default = None
@@ -34,13 +35,14 @@ ROUND_PRODUCT = 1
 NO_NEG_ZERO = 2
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
-    """Compile oracle.c into a shared library (plain gcc: no fast-math, no FMA contraction)."""
+def build(force: bool = True, src: str = _SRC, out: str = _LIB, kbit_src: str = _KBIT_SRC) -> str:
+    """Compile oracle.c and kbit.c into one shared library (plain gcc: no fast-math, no FMA
+    contraction). A test may pass its own copy of either source."""
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-           "-shared", "-pthread", src, "-o", tmp, "-lm"]
+           "-shared", "-pthread", src, kbit_src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -80,8 +82,91 @@ class Oracle:
         lib.oracle_addmm_bf16_points_ex.restype = ctypes.c_int
         lib.oracle_round_bf16_array.argtypes = [f64p, u16p, i64]
         lib.oracle_round_bf16_array.restype = None
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_e4m4_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m4_decode.restype = ctypes.c_double
+        lib.oracle_e4m4_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e4m4_encode.restype = ctypes.c_uint8
+        lib.oracle_nf_codebook.argtypes = [ctypes.c_int, f64p]
+        lib.oracle_nf_codebook.restype = ctypes.c_int
+        lib.oracle_kbit_quantize.argtypes = [f64p, i64, ctypes.c_int, f32p, u32p, u8p, f64p]
+        lib.oracle_kbit_quantize.restype = ctypes.c_int
+        lib.oracle_kbit_dequant.argtypes = [u32p, u8p, f32p, ctypes.c_int, i64, f64p]
+        lib.oracle_kbit_dequant.restype = ctypes.c_int
+        lib.oracle_kbit_gemv_bf16.argtypes = [u16p, u32p, u8p, f32p, ctypes.c_int, u16p, u16p, f64p,
+                                              i64, i64, i64]
+        lib.oracle_kbit_gemv_bf16.restype = ctypes.c_int
         self.lib = lib
         self.path = path
+
+    # ---------------------------------------------------------------- k-bit quantized GEMV
+
+    def e4m4_decode(self, codes) -> np.ndarray:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        return np.array([self.lib.oracle_e4m4_decode(int(c)) for c in codes.reshape(-1)],
+                        dtype=np.float64).reshape(codes.shape)
+
+    def e4m4_encode(self, values) -> np.ndarray:
+        values = np.ascontiguousarray(values, dtype=np.float64)
+        return np.array([self.lib.oracle_e4m4_encode(float(v)) for v in values.reshape(-1)],
+                        dtype=np.uint8).reshape(values.shape)
+
+    def nf_codebook(self, k: int) -> np.ndarray:
+        cb = np.empty(1 << k, dtype=np.float64)
+        if self.lib.oracle_nf_codebook(int(k), _ptr(cb, ctypes.c_double)) != 0:
+            raise ValueError("bad k")
+        return cb
+
+    def kbit_quantize(self, W, k: int, cb):
+        """W float64 [N, K] (K % 32 == 0) -> (planes uint32 [N, K/32, k], absmax E4M4 uint8
+        [N, K/32], unencoded absmax float64 [N, K/32])."""
+        W = np.ascontiguousarray(W, dtype=np.float64)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        N, K = W.shape
+        planes = np.empty((N, K // 32, k), dtype=np.uint32)
+        amax = np.empty((N, K // 32), dtype=np.uint8)
+        raw = np.empty((N, K // 32), dtype=np.float64)
+        rc = self.lib.oracle_kbit_quantize(_ptr(W, ctypes.c_double), W.size, int(k), _ptr(cb, ctypes.c_float),
+                                           _ptr(planes, ctypes.c_uint32), _ptr(amax, ctypes.c_uint8),
+                                           _ptr(raw, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_kbit_quantize: bad arguments")
+        return planes, amax, raw
+
+    def kbit_dequant(self, planes, absmax, cb, k: int) -> np.ndarray:
+        planes = np.ascontiguousarray(planes, dtype=np.uint32)
+        absmax = np.ascontiguousarray(absmax, dtype=np.uint8)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        N, B = absmax.shape
+        out = np.empty((N, B * 32), dtype=np.float64)
+        rc = self.lib.oracle_kbit_dequant(_ptr(planes, ctypes.c_uint32), _ptr(absmax, ctypes.c_uint8),
+                                          _ptr(cb, ctypes.c_float), int(k), out.size, _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_kbit_dequant: bad arguments")
+        return out
+
+    def kbit_gemv_bf16(self, X, planes, absmax, cb, k: int, R):
+        """Y = bf16(X @ What^T + R) with What the dequantized k-bit weights: (Y bits, exact sums)."""
+        X = _u16(X)
+        planes = np.ascontiguousarray(planes, dtype=np.uint32)
+        absmax = np.ascontiguousarray(absmax, dtype=np.uint8)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        M, K = X.shape
+        N = absmax.shape[0]
+        if absmax.shape != (N, K // 32) or planes.shape != (N, K // 32, k):
+            raise ValueError("planes [N, K/32, k] and absmax [N, K/32] expected")
+        R = _u16(R, (M, N))
+        Y = np.empty((M, N), dtype=np.uint16)
+        ACC = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_kbit_gemv_bf16(_ptr(X, ctypes.c_uint16), _ptr(planes, ctypes.c_uint32),
+                                            _ptr(absmax, ctypes.c_uint8), _ptr(cb, ctypes.c_float), int(k),
+                                            _ptr(R, ctypes.c_uint16), _ptr(Y, ctypes.c_uint16),
+                                            _ptr(ACC, ctypes.c_double), M, N, K)
+        if rc != 0:
+            raise ValueError("oracle_kbit_gemv_bf16: bad arguments")
+        return Y, ACC
 
     def addmm_bf16(self, X, W, R, threads: int | None = None, want_acc: bool = True, flags: int = 0):
         """Return (Y bits uint16[M,N], exact fp64 sums float64[M,N] or None). flags: ROUND_PRODUCT
@@ -164,3 +249,27 @@ def bf16_bits_to_f64(b) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float64 (bits << 16 read as binary32)."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def nf_codebook(k: int) -> np.ndarray:
+    return default().nf_codebook(k)
+
+
+def e4m4_decode(codes) -> np.ndarray:
+    return default().e4m4_decode(codes)
+
+
+def e4m4_encode(values) -> np.ndarray:
+    return default().e4m4_encode(values)
+
+
+def kbit_quantize(W, k: int, cb):
+    return default().kbit_quantize(W, k, cb)
+
+
+def kbit_dequant(planes, absmax, cb, k: int) -> np.ndarray:
+    return default().kbit_dequant(planes, absmax, cb, k)
+
+
+def kbit_gemv_bf16(X, planes, absmax, cb, k: int, R):
+    return default().kbit_gemv_bf16(X, planes, absmax, cb, k, R)
