@@ -21,6 +21,9 @@ Other modes write JSONL rows (one per configuration or M) to --out:
                   N = 7168/--shards columns for rank --rank, R and Y as column blocks of the
                   full-width matrices, two roundings and no -0, W rotated over >= 40 copies
   --mode shard-sweep   the same over every built configuration
+  --mode kbit     the k-bit quantized decode GEMV (bitsandbytes page "compare/main...QLORA-2.diff"),
+                  N = 7168, K = 3584, k in --kbits, M in --ms (default 1,2,4); the planes and
+                  scale bytes rotate over enough copies to exceed 308 MB
 """
 from __future__ import annotations
 
@@ -47,6 +50,12 @@ def algorithmic_bytes(M: int, N: int = None, K: int = None) -> int:
     N = N_DIM if N is None else N
     K = K_DIM if K is None else K
     return 2 * N * K + 2 * M * K + 2 * M * N + 2 * M * N
+
+
+def kbit_algorithmic_bytes(M: int, N: int, K: int, kbits: int) -> int:
+    """k bit-plane words and one scale byte per 32 weights read once, the 2^k-entry fp32
+    codebook, X and R read once, Y written once (bf16)."""
+    return N * (K // 32) * (4 * kbits + 1) + 4 * (1 << kbits) + 2 * M * K + 2 * M * N + 2 * M * N
 
 
 def lookup_traffic(cfg: dict, M: int):
@@ -156,6 +165,28 @@ class ShardWorkload:
         torch.cuda.synchronize()
         log("shard inputs M=%d N=%d (rank %d of %d) copies=%d ready in %.1fs (%.1f MB of W)" % (
             M, N, rank, shards, copies, time.time() - t0, copies * N * K * 2 / 1e6))
+
+
+class KbitWorkload:
+    """Device-resident k-bit GEMV inputs: one X and codebook, C copies of (planes, scales) and R."""
+
+    def __init__(self, M: int, copies: int, kbits: int, N: int = N_DIM, K: int = K_DIM):
+        import torch
+
+        from decode_skinny_addmm_amd import synth
+        t0 = time.time()
+        X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kbits, copies=copies)
+        self.host = (X, ps[0], As[0], rs[0], cb)
+        self.M, self.N, self.K, self.copies, self.kbits = M, N, K, copies, kbits
+        self.X = X.cuda()
+        self.cb = cb.cuda()
+        self.W = [(p.cuda(), a.cuda()) for p, a in zip(ps, As)]
+        self.R = [r.cuda() for r in rs]
+        self.Y = [torch.empty_like(r) for r in self.R]
+        del ps, As, rs
+        torch.cuda.synchronize()
+        log("kbit inputs M=%d k=%d copies=%d ready in %.1fs (%.1f MB of planes+scales)" % (
+            M, kbits, copies, time.time() - t0, copies * N * (K // 32) * (4 * kbits + 1) / 1e6))
 
 
 def time_graph(launch, wl, calls: int, warmup: int, steps: int):
@@ -521,6 +552,60 @@ def run_shard(args, sk):
         out.close()
 
 
+def run_kbit(args, sk):
+    """The k-bit quantized GEMV at N = 7168, K = 3584: per (k, M) one JSON row with the mean
+    launch time, algorithmic GB/s and roofline fraction, the dense bf16 kernel at the same M
+    for context, and a full comparison of copy 0 against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    Ms = [int(x) for x in args.ms.split(",")] if args.ms else [1, 2, 4]
+    kbs = [int(x) for x in args.kbits.split(",")]
+    out = open(args.out, "a") if args.out else None
+    for kb in kbs:
+        per_copy = N_DIM * (K_DIM // 32) * (4 * kb + 1)
+        copies = max(8, -(-308_000_000 // per_copy))
+        for M in Ms:
+            wl = KbitWorkload(M, copies, kb)
+
+            def launch(X, W, R, Y, wl=wl):
+                return sk.kbit_gemv(X, W[0], W[1], wl.cb, wl.kbits, R, out=Y)
+            row = {"mode": "kbit", "kbits": kb, "m": M, "n": N_DIM, "k": K_DIM, "copies": copies,
+                   "calls": args.calls}
+            try:
+                per, total_ms = time_graph(launch, wl, args.calls, args.warmup, args.steps)
+                us = [p / args.calls for p in per]
+                mean_us = total_ms * 1000.0 / (args.steps * args.calls)
+                nbytes = kbit_algorithmic_bytes(M, N_DIM, K_DIM, kb)
+                row.update(summarize(us))
+                row.update({"mean_us_total": mean_us, "gbs": nbytes / (mean_us * 1e-6) / 1e9,
+                            "frac_hbm": nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                            "bytes_per_launch": nbytes})
+                X, pl, am, R, cb = wl.host
+                Y = launch(wl.X, wl.W[0], wl.R[0], torch.empty_like(wl.R[0]))
+                torch.cuda.synchronize()
+                yo, _ = oracle.kbit_gemv_bf16(synth_bits(X), pl.numpy().view(np.uint32), am.numpy(), cb.numpy(),
+                                              kb, synth_bits(R))
+                row["matches_oracle_frac"] = float(np.mean(synth_bits(Y.cpu()) == yo))
+            except Exception as e:  # noqa: BLE001
+                row.update({"valid": False, "error": "%s: %s" % (type(e).__name__, e)})
+            line = json.dumps(row, sort_keys=True)
+            print(line, flush=True)
+            if out:
+                out.write(line + "\n")
+                out.flush()
+            del wl
+            torch.cuda.empty_cache()
+    if out:
+        out.close()
+
+
+def synth_bits(t):
+    from decode_skinny_addmm_amd import synth
+    return synth.bits(t)
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -530,10 +615,12 @@ def main():
     p.add_argument("--copies", type=int, default=6)
     p.add_argument("--calls", type=int, default=500, help="launches captured per graph (one step)")
     p.add_argument("--config", type=parse_config, default=None)
-    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib", "shard", "shard-sweep"),
+    p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib", "shard", "shard-sweep",
+                                        "kbit"),
                    default="default")
     p.add_argument("--shards", type=int, default=8, help="shard/shard-sweep: ranks the 7168 columns split over")
     p.add_argument("--rank", type=int, default=3, help="shard/shard-sweep: which rank's column block")
+    p.add_argument("--kbits", type=str, default="2,3,4,5", help="kbit: comma-separated bits per weight")
     p.add_argument("--out", type=str, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -564,6 +651,8 @@ def main():
         run_calib(args, sk)
     elif args.mode in ("shard", "shard-sweep"):
         run_shard(args, sk)
+    elif args.mode == "kbit":
+        run_kbit(args, sk)
     elif args.mode == "sweep":
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
         paths = {int(x) for x in args.paths.split(",")} if args.paths else None

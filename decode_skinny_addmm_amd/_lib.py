@@ -22,6 +22,7 @@ CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
             "skinny_addmm_bf16_acc_f32", "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
+            "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32",
             "skinny_num_configs", "skinny_get_config",
             "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
             "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy")
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.skinny_addmm_bf16_shard.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_uint32, cfgp, vp]
     L.skinny_addmm_bf16_shard_acc_f32.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_uint32,
                                                   cfgp, vp]
+    L.skinny_kbit_gemv_bf16.argtypes = [vp, vp, vp, vp, ctypes.c_int32, vp, vp, i64, i64, i64, vp]
+    L.skinny_kbit_gemv_bf16_acc_f32.argtypes = [vp, vp, vp, vp, ctypes.c_int32, vp, vp, i64, i64, i64, vp]
     L.skinny_select_config.argtypes = [i64, i64, i64, cfgp]
     L.skinny_get_config.argtypes = [ctypes.c_int32, cfgp]
     L.skinny_config_resources.argtypes = [cfgp, ctypes.POINTER(SkinnyResources)]
@@ -88,6 +91,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, f).restype = ctypes.c_int
     for f in ("skinny_addmm_bf16", "skinny_addmm_bf16_with_config", "skinny_addmm_bf16_acc_f32",
               "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
+              "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32",
               "skinny_select_config", "skinny_get_config", "skinny_config_resources",
               "skinny_num_configs", "skinny_last_hip_error"):
         getattr(L, f).restype = ctypes.c_int

@@ -133,10 +133,45 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
     return SKINNY_OK;
 }
 
+skinny_status run_kbit(const void *X, const uint32_t *planes, const uint8_t *absmax, const float *codebook,
+                       int32_t kbits, const void *R, void *out, bool acc_out, int64_t M, int64_t N, int64_t K,
+                       void *stream) {
+    if (M < 0 || N < 0 || K < 0 || kbits < 2 || kbits > 5) return SKINNY_EINVAL;
+    if (K % 32 != 0 || K > kbit_max_k()) return SKINNY_ENOTSUP;
+    if (M == 0 || N == 0) return SKINNY_OK;
+    if (!R || !out) return SKINNY_EINVAL;
+    if (K > 0 && (!X || !planes || !absmax)) return SKINNY_EINVAL;
+    if (!codebook) return SKINNY_EINVAL;
+    if ((X && !aligned(X, 16)) || (planes && !aligned(planes, 4)) || !aligned(codebook, 4) ||
+        !aligned(R, 2) || !aligned(out, acc_out ? 4 : 2))
+        return SKINNY_EALIGN;
+    if (M > INT_MAX || N > INT_MAX || (M + 3) / 4 > 65535) return SKINNY_ENOTSUP;
+    KbitArgs a{static_cast<const uint16_t *>(X), planes, absmax, codebook, kbits,
+               static_cast<const uint16_t *>(R), out, M, N, K, acc_out, static_cast<hipStream_t>(stream)};
+    const hipError_t err = launch_kbit_gemv(a);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return SKINNY_EHIP;
+    }
+    return SKINNY_OK;
+}
+
 }  // namespace
 }  // namespace skinny
 
 extern "C" {
+
+skinny_status skinny_kbit_gemv_bf16(const void *X, const uint32_t *planes, const uint8_t *absmax,
+                                    const float *codebook, int32_t kbits, const void *R, void *Y,
+                                    int64_t M, int64_t N, int64_t K, void *stream) {
+    return skinny::run_kbit(X, planes, absmax, codebook, kbits, R, Y, false, M, N, K, stream);
+}
+
+skinny_status skinny_kbit_gemv_bf16_acc_f32(const void *X, const uint32_t *planes, const uint8_t *absmax,
+                                            const float *codebook, int32_t kbits, const void *R, float *ACC,
+                                            int64_t M, int64_t N, int64_t K, void *stream) {
+    return skinny::run_kbit(X, planes, absmax, codebook, kbits, R, ACC, true, M, N, K, stream);
+}
 
 skinny_status skinny_addmm_bf16(const void *X, const void *W, const void *R, void *Y, int64_t M,
                                 int64_t N, int64_t K, void *stream) {

@@ -49,6 +49,22 @@ struct KernelEntry {
     int32_t k_align = 8;            // K must be a multiple of this
 };
 
+// Arguments of one k-bit quantized GEMV call (kbit_gemv.hip), validated by the C ABI layer.
+struct KbitArgs {
+    const uint16_t *X;        // bf16 [M, K]
+    const uint32_t *planes;   // [N, K/32, kbits] bit-plane words
+    const uint8_t *absmax;    // [N, K/32] E4M4 bytes
+    const float *codebook;    // [2^kbits]
+    int kbits;                // 2 .. 5
+    const uint16_t *R;        // bf16 [M, N]
+    void *out;                // bf16 Y or float ACC [M, N]
+    int64_t M, N, K;
+    bool acc_out;
+    hipStream_t stream;
+};
+hipError_t launch_kbit_gemv(const KbitArgs &a);
+int64_t kbit_max_k();
+
 // Registries filled by each kernel family's translation unit.
 const KernelEntry *gemv_entries(int *count);
 const KernelEntry *mfma_entries(int *count);

@@ -170,6 +170,58 @@ def addmm_shard_acc_f32(X, W, R, out=None, round_product=False, config=None, str
     return out
 
 
+def _check_kbit(X, planes, absmax, codebook, kbits, R, out, out_dtype):
+    for name, t in (("X", X), ("planes", planes), ("absmax", absmax), ("codebook", codebook), ("R", R),
+                    ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if X.dtype != torch.bfloat16 or R.dtype != torch.bfloat16 or out.dtype != out_dtype:
+        raise ValueError("X and R must be bfloat16, out %s" % out_dtype)
+    if planes.dtype not in (torch.int32, torch.uint32) or absmax.dtype != torch.uint8 or codebook.dtype != torch.float32:
+        raise ValueError("planes must be int32/uint32 bit words, absmax uint8, codebook float32")
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M, K = X.shape
+    N = R.shape[0 if R.dim() == 1 else 1]
+    if tuple(planes.shape) != (N, K // 32, kbits) or tuple(absmax.shape) != (N, K // 32):
+        raise ValueError("planes must be [N, K/32, kbits] and absmax [N, K/32]")
+    if tuple(codebook.shape) != (1 << kbits,):
+        raise ValueError("codebook must have 2^kbits entries")
+    if tuple(R.shape) != (M, N) or tuple(out.shape) != (M, N):
+        raise ValueError("R and out must be [M, N]")
+    return M, N, K
+
+
+def kbit_gemv(X, planes, absmax, codebook, kbits: int, R, out=None, stream=None) -> torch.Tensor:
+    """Y = bf16(X @ What^T + R) with What the k-bit quantized weights (skinny_kbit_gemv_bf16)."""
+    if out is None:
+        out = torch.empty_like(R)
+    M, N, K = _check_kbit(X, planes, absmax, codebook, kbits, R, out, torch.bfloat16)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_kbit_gemv_bf16(X.data_ptr(), planes.data_ptr(), absmax.data_ptr(), codebook.data_ptr(),
+                                         int(kbits), R.data_ptr(), out.data_ptr(), M, N, K,
+                                         _stream_ptr(stream, X.device))
+    check(st, "skinny_kbit_gemv_bf16")
+    return out
+
+
+def kbit_gemv_acc_f32(X, planes, absmax, codebook, kbits: int, R, out=None, stream=None) -> torch.Tensor:
+    """Test entry: the fp32 value each output of kbit_gemv is rounded from."""
+    if out is None:
+        out = torch.empty(R.shape, dtype=torch.float32, device=R.device)
+    M, N, K = _check_kbit(X, planes, absmax, codebook, kbits, R, out, torch.float32)
+    with torch.cuda.device(X.device):
+        st = lib().skinny_kbit_gemv_bf16_acc_f32(X.data_ptr(), planes.data_ptr(), absmax.data_ptr(),
+                                                 codebook.data_ptr(), int(kbits), R.data_ptr(), out.data_ptr(),
+                                                 M, N, K, _stream_ptr(stream, X.device))
+    check(st, "skinny_kbit_gemv_bf16_acc_f32")
+    return out
+
+
 def select_config(M: int, N: int = 7168, K: int = 3584) -> dict:
     c = SkinnyConfig()
     check(lib().skinny_select_config(M, N, K, ctypes.byref(c)), "skinny_select_config")

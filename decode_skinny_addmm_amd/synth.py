@@ -73,3 +73,28 @@ def small_int_inputs(M: int, N: int, K: int, seed: int = 7):
     W = (((n + 3 * k) % 5) - 2).to(torch.bfloat16)
     R = torch.randint(-8, 9, (M, N), generator=g).to(torch.bfloat16)
     return X, W, R
+
+
+# ---- k-bit quantized weights (random bit patterns; no quantization arithmetic) ------
+
+def make_kbit_inputs(M: int, N: int = N_DEFAULT, K: int = K_DEFAULT, kbits: int = 4, copies: int = 1,
+                     seed: int | None = None):
+    """Inputs of the k-bit quantized GEMV, drawn as raw bits (the GEMV takes any bits):
+    X bf16 [M, K] ~ N(0,1); per copy, plane words int32 [N, K/32, kbits] (uniform random
+    bits, i.e. uniform codebook indices), scale bytes uint8 [N, K/32] uniform in
+    [0x60, 0x68) (E4M4 values 1/32 .. 1.44/32: the block maximum of N(0,1)/sqrt(3584)
+    weights is about 0.04, so the product keeps the unit scale of the dense inputs),
+    R bf16 [M, N] ~ N(0,1); and a codebook of
+    2^kbits sorted float32 levels: -1, +1 and uniform draws in between.
+    Returns (X, [planes], [absmax], [R], codebook)."""
+    g = generator(M, 7919 + kbits if seed is None else seed)
+    X = torch.randn((M, K), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    planes, scales = [], []
+    for _ in range(copies):
+        planes.append(torch.randint(-2 ** 31, 2 ** 31, (N, K // 32, kbits), generator=g, dtype=torch.int64)
+                      .to(torch.int32))
+        scales.append(torch.randint(0x60, 0x68, (N, K // 32), generator=g, dtype=torch.int64).to(torch.uint8))
+    rs = [torch.randn((M, N), generator=g, dtype=torch.float32).to(torch.bfloat16) for _ in range(copies)]
+    inner = torch.rand((2 ** kbits - 2,), generator=g, dtype=torch.float32) * 2 - 1
+    codebook = torch.cat([torch.tensor([-1.0]), inner.sort().values, torch.tensor([1.0])])
+    return X, planes, scales, rs, codebook

@@ -169,6 +169,36 @@ SKINNY_API skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const vo
                                                          int64_t M, int64_t N, int64_t K, uint32_t flags,
                                                          const skinny_config *cfg, void *stream);
 
+/*
+ * Decode GEMV with k-bit quantized weights (the bitsandbytes page "compare/main...QLORA-2.diff":
+ * agents/kbit_gemm_context.md sections 1.2-1.6 for the format, its QLoRA guide's section 7 for
+ * the scalar decode GEMV):
+ *
+ *     Y[m, n] = bf16( sum_k X[m, k] * What[n, k]  +  R[m, n] ),
+ *     What[n, k] = codebook[idx(n, k)] * e4m4(absmax[n, k / 32])
+ *
+ *   X        bf16 [M, K] row-major, 16-byte aligned
+ *   planes   uint32 [N, K/32, kbits]: for the 32-element block (n, b), word i holds bit i of the
+ *            indices of its elements (bit j of the word = element j); 4-byte aligned
+ *   absmax   uint8 [N, K/32]: the block scale in E4M4 (4-bit exponent, bias 11, 4-bit
+ *            mantissa: e > 0 gives 2^(e-11) * (1 + m/16), e == 0 gives m * 2^-14)
+ *   codebook float [2^kbits] (e.g. the normal-float levels); 4-byte aligned
+ *   R, Y     bf16 [M, N] row-major (Y may be exactly R)
+ * kbits is 2..5 (else SKINNY_EINVAL); K must be a multiple of 32 and at most 9824 (X is held
+ * in LDS), else SKINNY_ENOTSUP. Sums are fp32, one RNE rounding. M of any size runs in passes
+ * of up to 4 rows (the kernel is meant for decode, M <= 4). Same conventions as above
+ * otherwise (device pointers, asynchronous, no allocation).
+ */
+SKINNY_API skinny_status skinny_kbit_gemv_bf16(const void *X, const uint32_t *planes, const uint8_t *absmax,
+                                               const float *codebook, int32_t kbits, const void *R, void *Y,
+                                               int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Test entry: the fp32 value each output is rounded from, fp32(sum) + fp32(R), to ACC [M, N]. */
+SKINNY_API skinny_status skinny_kbit_gemv_bf16_acc_f32(const void *X, const uint32_t *planes,
+                                                       const uint8_t *absmax, const float *codebook,
+                                                       int32_t kbits, const void *R, float *ACC,
+                                                       int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Number of configurations built into the library, and the i-th of them (0-based). */
 SKINNY_API int32_t skinny_num_configs(void);
 SKINNY_API skinny_status skinny_get_config(int32_t index, skinny_config *out);

@@ -147,3 +147,25 @@ def test_shard_argument_checks(L, ldr, ldy, M, flags, out_is_r, expect):
     if not out_is_r:  # the fp32 test output never aliases R
         assert L.skinny_addmm_bf16_shard_acc_f32(A16, A16, A16, ldr, A16 + 0x1000, ldy, M, 8, 8, flags,
                                                  None, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, A16, A16, 1, A16, A16, 1, 8, 64), 1),      # kbits below 2
+    ((A16, A16, A16, A16, 6, A16, A16, 1, 8, 64), 1),      # kbits above 5
+    ((A16, A16, A16, A16, 4, A16, A16, -1, 8, 64), 1),     # negative M
+    ((A16, A16, A16, A16, 4, A16, A16, 1, 8, 48), 3),      # K % 32 != 0
+    ((A16, A16, A16, A16, 4, A16, A16, 1, 8, 32 * 400), 3),  # K beyond the X staging limit
+    ((A16, A16, A16, None, 4, A16, A16, 1, 8, 64), 1),     # NULL codebook
+    ((None, A16, A16, A16, 4, A16, A16, 1, 8, 64), 1),     # NULL X with K > 0
+    ((A16, None, A16, A16, 4, A16, A16, 1, 8, 64), 1),     # NULL planes with K > 0
+    ((A16, A16, A16, A16, 4, None, A16, 1, 8, 64), 1),     # NULL residual
+    ((A16 + 8, A16, A16, A16, 4, A16, A16, 1, 8, 64), 2),  # X not 16-byte aligned
+    ((A16, A16 + 2, A16, A16, 4, A16, A16, 1, 8, 64), 2),  # plane words not 4-byte aligned
+    ((A16, A16, A16, A16 + 2, 4, A16, A16, 1, 8, 64), 2),  # codebook not 4-byte aligned
+    ((A16, A16, A16, A16, 4, A2 + 1, A16, 1, 8, 64), 2),   # R odd address
+    ((None, None, None, A16, 4, None, None, 0, 8, 64), 0),  # M == 0: no-op
+])
+def test_kbit_argument_checks(L, args, expect):
+    assert L.skinny_kbit_gemv_bf16(*args, None) == expect
+    if args[6] is not None:
+        assert L.skinny_kbit_gemv_bf16_acc_f32(*args, None) == expect
