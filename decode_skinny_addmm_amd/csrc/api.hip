@@ -146,6 +146,8 @@ skinny_status run_kbit(const void *X, const uint32_t *planes, const uint8_t *abs
         !aligned(R, 2) || !aligned(out, acc_out ? 4 : 2))
         return SKINNY_EALIGN;
     if (M > INT_MAX || N > INT_MAX || (M + 3) / 4 > 65535) return SKINNY_ENOTSUP;
+    // K == 0: no weights, Y = R; the dense kernels' empty-K path does exactly that
+    if (K == 0) return run(X, nullptr, R, N, out, N, acc_out, M, N, 0, 0u, nullptr, stream);
     KbitArgs a{static_cast<const uint16_t *>(X), planes, absmax, codebook, kbits,
                static_cast<const uint16_t *>(R), out, M, N, K, acc_out, static_cast<hipStream_t>(stream)};
     const hipError_t err = launch_kbit_gemv(a);

@@ -2,33 +2,38 @@
 //
 // Format (the bitsandbytes page "compare/main...QLORA-2.diff", agents/kbit_gemm_context.md,
 // sections 1.3-1.6): W is stored in blocks of 32 consecutive elements of a row; a block has
-// k bit-plane words (bit j of word b = bit b of element j's codebook index) and one E4M4
+// k bit-plane words (bit j of word i = bit i of element j's codebook index) and one E4M4
 // absmax byte (4-bit exponent with bias 11, 4-bit mantissa); the dequantized weight is
 // codebook[index] * decode(absmax). The GEMV is that page's decode kernel ("Kernel 1: Scalar
 // GEMV" of its QLoRA guide, section 7), here with this library's bf16 X, R and Y.
 //
-// Design for gfx950:
-//   * a workgroup is 4 waves; a wave takes 4 rows of W at a time, 16 lanes per row, and
-//     lane s of a row group walks the row's blocks s, s + 16, ...; so each lane stays on one
-//     row, the 16 lanes of a group read 16 neighbouring blocks (contiguous plane words), and
-//     the row's partial sums meet in a 16-lane DPP reduction;
-//   * X (M <= MT rows) is copied to LDS once per workgroup with a 16-byte pad after every
-//     32-element block, so the 16 lanes of a group (64-byte stride) read distinct banks;
-//   * the codebook (2^k fp32 entries) sits in LDS: one ds_read_b32 per element, conflict-free
-//     because the whole table spans fewer than 64 banks;
-//   * per block: the k plane words and the scale byte are loaded together for U blocks
-//     ahead; an element's index is assembled from bit j of each plane; the 32 products of a
-//     block are summed in fp32 and scaled once by the decoded absmax;
-//   * R is prefetched by the lanes that write; one RNE rounding to bf16 at the end.
+// At M <= 4 the work per weight, not the bytes, sets the time (about 0.5 byte per weight at
+// k = 4 against one codebook lookup and one FMA per weight and output row), so the design
+// minimises VALU instructions per weight on gfx950:
+//   * a lane owns one block position b of the K axis for the whole launch: the 32 X values
+//     of that block (per output row) are converted to fp32 once and stay in VGPRs; the
+//     workgroup's lanes cover r rows x K/32 blocks, and walk G such row groups;
+//   * index decode without per-bit work: each plane word is rotated once so plane i lands on
+//     bit i + 2 of a byte; for each c = 0..7 one AND-OR per plane collects elements
+//     c, c+8, c+16, c+24 into one word whose bytes are the four indices times 4, i.e. the
+//     LDS byte addresses of their codebook entries; one rotation re-aligns the word; one
+//     bit-field extract per element feeds a ds_read_b32 (the 2^k-entry fp32 table spans at
+//     most 32 banks, so every lookup is conflict-free);
+//   * one fp32 FMA per weight and row; the block's sum is scaled once by its decoded absmax;
+//   * per-block partial sums meet in LDS; 16 lanes per output row add them and write
+//     bf16(sum + R) with one rounding (R is loaded by the writing lane at kernel start).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace skinny {
 namespace {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPadBlockBytes = 80;   // 64 bytes of a 32-element bf16 block + 16 bytes of padding
-constexpr int kUnroll = 4;           // blocks in flight per lane
+constexpr int kMaxThreads = 512;    // 2 waves per SIMD: up to 256 VGPRs (X of 4 rows takes 128)
+constexpr int kMaxRowGroups = 8;        // G: row groups a workgroup walks (plane words kept in flight)
+constexpr int kPartialBytes = 64 * 1024;  // LDS budget of the per-block partial sums
 
 // E4M4 byte -> fp32 (the page's decoder): e > 0: 2^(e - 11) * (1 + m/16) built as IEEE bits;
 // e == 0: m * 2^-14 (zero for m == 0).
@@ -39,109 +44,252 @@ __device__ __forceinline__ float e4m4_decode(uint32_t byte) {
     return e ? normal : sub;
 }
 
-// MT: rows of X per pass; KB: bits per index.
+__device__ __forceinline__ uint32_t rotr(uint32_t v, int s) { return __builtin_amdgcn_alignbit(v, v, s); }
+
+// (a & m) | acc as one VOP3 instruction (left to itself the compiler splits a chain of these
+// into ANDs and a three-input OR, one instruction more per word)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t acc) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(acc));
+    return d;
+}
+
+constexpr uint32_t rotl_c(uint32_t v, int s) { return s == 0 ? v : (v << s) | (v >> (32 - s)); }
+
+// Sum over the 16 lanes of a row of the wavefront (DPP row rotations stay within the row).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // ror 8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // ror 4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // ror 2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // ror 1
+    return v;
+}
+
+// Partial sum of one block for MT rows: decode the 32 indices of the block from its plane
+// words and accumulate x * codebook[index] (scaled by the block's absmax at the end).
+template <int KB, int MT>
+__device__ __forceinline__ void block_dot(const uint32_t (&P)[KB], uint32_t a, const float (&x)[MT][32],
+                                          const uint32_t (&msk)[8], const char *cbb, float (&out)[MT]) {
+    uint32_t Q[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) Q[i] = rotr(P[i], 30 - i);   // element j, plane i -> bit j + 2 + i
+    float s[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        // elements c + 8t (t = 0..3): their plane-i bits sit at 8t + 2 + i + c (mod 32)
+        // mask of plane i for this c: bit 2 + i of every byte rotated by c, i.e. msk[(c + i) % 8]
+        uint32_t w = Q[0] & msk[c];
+#pragma unroll
+        for (int i = 1; i < KB; ++i) w = and_or(Q[i], msk[(c + i) & 7], w);
+        if (c) w = rotr(w, c);                                   // byte t = 4 * index(c + 8t)
+        // hide w's known-zero bits so each byte is taken with one bit-field extract
+        // instead of a shift and a mask
+        asm("" : "+v"(w));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float cv = *reinterpret_cast<const float *>(cbb + ((w >> (8 * t)) & 0xFFu));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) s[m] = fmaf(x[m][c + 8 * t], cv, s[m]);
+        }
+    }
+    const float scale = e4m4_decode(a);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
+}
+
+// One launch: grid.x = ceil(N / (r * G)), grid.y = ceil(M / MT); blockDim.x = T (a multiple of
+// 64 with r * BPR <= T and r * G <= T / 16); K >= 32. Lane t < r * BPR owns row offset t / BPR and
+// block t % BPR; the other lanes compute a clamped copy that is not stored, and help with the
+// final sums.
 template <int KB, int MT, bool ACC>
-__global__ __launch_bounds__(256) void kbit_gemv_kernel(const uint16_t *__restrict__ X,
-                                                        const uint32_t *__restrict__ planes,
-                                                        const uint8_t *__restrict__ absmax,
-                                                        const float *__restrict__ codebook,
-                                                        const uint16_t *R, void *out, int M, int N, int K,
-                                                        Epilogue ep) {
+__global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *__restrict__ X,
+                                                                const uint32_t *__restrict__ planes,
+                                                                const uint8_t *__restrict__ absmax,
+                                                                const float *__restrict__ codebook,
+                                                                const uint16_t *R, void *out, int M, int N, int K,
+                                                                int r, int G) {
     constexpr int L = 1 << KB;
-    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [MT][BPR] padded blocks
     __shared__ float cbs[L];
+    extern __shared__ float part[];        // [r * G][MT][BPR]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int BPR = K >> 5;                                  // blocks per row
+    const int tid = threadIdx.x;
+    const int BPR = K >> 5;
+    const int rows = r * G;                  // rows of W this workgroup covers
+    const int n0 = blockIdx.x * rows;
     const int m0 = blockIdx.y * MT;
-    const int n = blockIdx.x * 16 + wave * 4 + (lane >> 4);  // this lane's row of W
-    const int s = lane & 15;                                 // position in the row group
-    const int nc = min(n, N - 1);                            // rows past N: computed, not stored
+    const bool active = tid < r * BPR;
+    const int roff = active ? tid / BPR : 0;
+    const int blk = active ? tid - roff * BPR : 0;
 
-    // residual of the output this lane writes (lanes s = (16/MT)*m of a group write row m)
-    constexpr int WSTEP = 16 / MT;
-    const int my_m = s / WSTEP;
-    const bool writer = (s % WSTEP) == 0;
-    const float rres = bf16_bits_to_f32(R[(size_t)min(m0 + my_m, M - 1) * ep.ldr + nc]);
+    // every load is unconditional (clamped addresses) and issued before the first wait, in
+    // the order the data is needed (the memory counter is waited on in issue order): X of this
+    // lane's block, the writer lanes' residuals, then the plane words and scale bytes of all
+    // kMaxRowGroups row groups (groups past G repeat group G - 1 and are not used). The
+    // codebook load is issued first.
+    const int lane = tid & 63;
+    float cbv = codebook[lane & (L - 1)];
+    asm volatile("" ::: "memory");             // the codebook load stays first
+    u32x4 xv[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint16_t *xr = X + (size_t)min(m0 + m, M - 1) * K + blk * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[m][q] = *reinterpret_cast<const u32x4 *>(xr + q * 8);
+    }
+    const int grp = tid >> 4, s16 = tid & 15;   // writer lanes: 16 per local row
+    const int wn = n0 + grp;
+    uint16_t rbits[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) rbits[m] = R[(size_t)min(m0 + m, M - 1) * N + min(wn, N - 1)];
 
-    if (tid < L) cbs[tid] = codebook[tid];
-    // X rows m0 .. m0+MT-1 (clamped) into LDS, 16 bytes per thread per step
-    const int chunks = MT * BPR * 4;
-    for (int c = tid; c < chunks; c += 256) {
-        const int m = c / (BPR * 4), r = c % (BPR * 4);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + (size_t)min(m0 + m, M - 1) * K + r * 8);
-        *reinterpret_cast<u32x4_t *>(xs + (m * BPR + (r >> 2)) * kPadBlockBytes + (r & 3) * 16) = v;
+    uint32_t P[kMaxRowGroups][KB];
+    uint32_t A[kMaxRowGroups];
+#pragma unroll
+    for (int g = 0; g < kMaxRowGroups; ++g) {
+        const int n = min(n0 + min(g, G - 1) * r + roff, N - 1);
+        const size_t b = (size_t)n * BPR + blk;
+#pragma unroll
+        for (int i = 0; i < KB; ++i) P[g][i] = __builtin_nontemporal_load(planes + b * KB + i);
+        A[g] = absmax[b];
+    }
+
+    // every wave writes the whole codebook itself (all waves write identical values), so
+    // its lookups need no workgroup barrier; the asm (with a memory clobber) keeps this after
+    // the loads above, so that its wait counts only the codebook load
+    asm volatile("" : "+v"(cbv) :: "memory");
+    if (lane < L) cbs[lane] = cbv;
+    uint32_t msk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        msk[j] = rotl_c(0x04040404u, j);
+        asm("" : "+v"(msk[j]));                  // keep in VGPRs: a VOP3 AND-OR takes no literal
+    }
+    // X to fp32: pinning xv here keeps its wait (and the conversion) from being scheduled
+    // between the loads above, where it would hold back their issue
+    float x[MT][32];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            asm volatile("" : "+v"(xv[m][q]));
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x[m][q * 8 + 2 * h] = __uint_as_float(xv[m][q][h] << 16);
+                x[m][q * 8 + 2 * h + 1] = __uint_as_float(xv[m][q][h] & 0xFFFF0000u);
+            }
+        }
+
+    const char *cbb = reinterpret_cast<const char *>(cbs);
+    // two row groups per step, so that their lookups and FMAs interleave; the empty asm
+    // pins each group's words to its step, so that the compiler cannot hoist their decode
+    // (and the wait for their loads) above the barrier and the groups before
+#pragma unroll
+    for (int g = 0; g < kMaxRowGroups; g += 2) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) asm volatile("" : "+v"(P[g][i]), "+v"(P[g + 1][i]));
+        asm volatile("" : "+v"(A[g]), "+v"(A[g + 1]));
+        if (g + 1 < G) {
+            float o0[MT], o1[MT];
+            block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
+            block_dot<KB, MT>(P[g + 1], A[g + 1], x, msk, cbb, o1);
+            if (active) {
+                float *p0 = part + (size_t)(g * r + roff) * MT * BPR + blk;
+                float *p1 = p0 + (size_t)r * MT * BPR;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    p0[m * BPR] = o0[m];
+                    p1[m * BPR] = o1[m];
+                }
+            }
+        } else if (g < G) {
+            float o0[MT];
+            block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
+            if (active) {
+                float *p0 = part + (size_t)(g * r + roff) * MT * BPR + blk;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) p0[m * BPR] = o0[m];
+            }
+        }
     }
     __syncthreads();
 
-    const uint32_t *prow = planes + (size_t)nc * BPR * KB;
-    const uint8_t *arow = absmax + (size_t)nc * BPR;
-    float acc[MT];
+    // 16 lanes per local row: add the row's BPR partial sums, one rounding with R
+    if (grp < rows) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-
-    // every lane runs the same trip count (blocks past the row are clamped and weighted 0)
-    for (int base = 0; base < BPR; base += 16 * kUnroll) {
-        const int b0 = base + s;
-        uint32_t w[kUnroll][KB];
-        uint32_t a[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int b = min(b0 + 16 * u, BPR - 1);         // clamped; masked below
-#pragma unroll
-            for (int i = 0; i < KB; ++i) w[u][i] = __builtin_nontemporal_load(prow + (size_t)b * KB + i);
-            a[u] = arow[b];
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int b = b0 + 16 * u;
-            const float scale = b < BPR ? e4m4_decode(a[u]) : 0.0f;   // past the row: adds 0
-            const int bx = min(b, BPR - 1);
-            float part[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) part[m] = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {                   // 8 elements per 16-byte chunk of X
-                u32x4_t xv[MT];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    xv[m] = *reinterpret_cast<const u32x4_t *>(xs + (m * BPR + bx) * kPadBlockBytes + q * 16);
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int j = q * 8 + t;
-                    uint32_t idx = 0;
-#pragma unroll
-                    for (int i = 0; i < KB; ++i) idx |= ((w[u][i] >> j) & 1u) << i;
-                    const float c = cbs[idx];
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        const uint32_t pair = xv[m][t >> 1];
-                        const float x = __uint_as_float((t & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
-                        part[m] = fmaf(x, c, part[m]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = fmaf(part[m], scale, acc[m]);
+        for (int m = 0; m < MT; ++m) {
+            const float *pr = part + (size_t)grp * MT * BPR + m * BPR;
+            float v = 0.0f;
+            for (int b = s16; b < BPR; b += 16) v += pr[b];
+            v = row16_sum(v);
+            if (s16 == 0 && wn < N && m0 + m < M) store_output<ACC>(out, Epilogue{N, N, 0u}, m0 + m, wn, v, bf16_bits_to_f32(rbits[m]));
         }
     }
+}
 
-    // sum over the 16 lanes of the row group; afterwards lane s holds row m = s / WSTEP in acc[0]
-    wave_transpose_reduce<MT, 8>(acc, lane);
-    if (writer && n < N && m0 + my_m < M) store_output<ACC>(out, ep, m0 + my_m, n, acc[0], rres);
+struct KbitShape {
+    int r, T, G;
+    size_t shmem;
+};
+
+// Rows per row group r and workgroup size T (a multiple of 64 holding r * BPR owner lanes and
+// 16 writer lanes per row): the fewest idle SIMD lanes first (waves are counted in rounds of
+// four, one per SIMD), then a size of 256..512 lanes, then the smaller size. G row groups per workgroup so that every local row has a writer group, the
+// partial sums fit their LDS budget and the grid still covers the chip.
+KbitShape kbit_shape(int64_t N, int64_t K, int MT) {
+    const int BPR = (int)(K / 32);
+    KbitShape s{16, 256, 1, 0};
+    if (BPR > 0) {
+        double best_eff = -1.0;
+        int best_pen = 2;
+        for (int r = 1; r * BPR <= kMaxThreads && 16 * r <= kMaxThreads; ++r) {
+            const int T = ((std::max(r * BPR, 16 * r) + 63) / 64) * 64;
+            // a CU runs a workgroup's waves on its 4 SIMDs: T / 64 waves take the time of a
+            // multiple of 4 of them, so count lanes against whole rounds of 4 waves
+            const int slots = ((T / 64 + 3) / 4) * 4 * 64;
+            const double eff = (double)(r * BPR) / slots;
+            const int pen = (T >= 256 && T <= 512) ? 0 : 1;
+            const bool better = eff > best_eff + 1e-9 ||
+                                (eff > best_eff - 1e-9 && (pen < best_pen || (pen == best_pen && T < s.T)));
+            if (better) {
+                best_eff = eff;
+                best_pen = pen;
+                s.r = r;
+                s.T = T;
+            }
+        }
+    }
+    // G: the row groups a workgroup walks. Each of the 256 CUs takes ceil(WGs / 256) workgroups
+    // of G groups; pick the G with the least such work per CU, the largest on a tie (fewer,
+    // longer workgroups pay the load latency at their start fewer times).
+    const int64_t groups = (N + s.r - 1) / s.r;
+    int Gmax = std::min(kMaxRowGroups, std::max(1, (s.T / 16) / s.r));
+    if (BPR > 0) Gmax = std::min(Gmax, std::max(1, kPartialBytes / (s.r * MT * BPR * 4)));
+    int64_t best = -1;
+    for (int G = 1; G <= Gmax; ++G) {
+        const int64_t wgs = (groups + G - 1) / G;
+        const int64_t cost = ((wgs + 255) / 256) * G;
+        if (best < 0 || cost <= best) {
+            best = cost;
+            s.G = G;
+        }
+    }
+    s.shmem = (size_t)s.r * s.G * MT * std::max(BPR, 1) * sizeof(float);
+    return s;
 }
 
 template <int KB, int MT>
 hipError_t launch_kbit(const KbitArgs &a) {
-    dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + MT - 1) / MT));
-    const size_t shmem = (size_t)MT * (a.K / 32) * kPadBlockBytes;
-    const Epilogue ep{(int)a.N, (int)a.N, 0u};
+    const KbitShape s = kbit_shape(a.N, a.K, MT);
+    const int rows = s.r * s.G;
+    dim3 grid((unsigned)((a.N + rows - 1) / rows), (unsigned)((a.M + MT - 1) / MT));
     if (a.acc_out)
-        hipLaunchKernelGGL((kbit_gemv_kernel<KB, MT, true>), grid, dim3(256), shmem, a.stream, a.X, a.planes,
-                           a.absmax, a.codebook, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, ep);
+        hipLaunchKernelGGL((kbit_gemv_kernel<KB, MT, true>), grid, dim3(s.T), s.shmem, a.stream, a.X, a.planes,
+                           a.absmax, a.codebook, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, s.r, s.G);
     else
-        hipLaunchKernelGGL((kbit_gemv_kernel<KB, MT, false>), grid, dim3(256), shmem, a.stream, a.X, a.planes,
-                           a.absmax, a.codebook, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, ep);
+        hipLaunchKernelGGL((kbit_gemv_kernel<KB, MT, false>), grid, dim3(s.T), s.shmem, a.stream, a.X, a.planes,
+                           a.absmax, a.codebook, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, s.r, s.G);
     return hipGetLastError();
 }
 
@@ -155,8 +303,8 @@ hipError_t launch_kbit_mt(const KbitArgs &a) {
 }  // namespace
 
 int64_t kbit_max_k() {
-    // X of 4 rows in padded LDS blocks: 4 * (K / 32) * 80 bytes, kept within 96 KB
-    return (int64_t)(96 * 1024 / (4 * kPadBlockBytes)) * 32;
+    // one lane per 32-element block of a row, at most kMaxThreads lanes per workgroup
+    return (int64_t)kMaxThreads * 32;
 }
 
 hipError_t launch_kbit_gemv(const KbitArgs &a) {

@@ -184,8 +184,8 @@ SKINNY_API skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const vo
  *            mantissa: e > 0 gives 2^(e-11) * (1 + m/16), e == 0 gives m * 2^-14)
  *   codebook float [2^kbits] (e.g. the normal-float levels); 4-byte aligned
  *   R, Y     bf16 [M, N] row-major (Y may be exactly R)
- * kbits is 2..5 (else SKINNY_EINVAL); K must be a multiple of 32 and at most 9824 (X is held
- * in LDS), else SKINNY_ENOTSUP. Sums are fp32, one RNE rounding. M of any size runs in passes
+ * kbits is 2..5 (else SKINNY_EINVAL); K must be a multiple of 32 and at most 16384 (one lane
+ * per 32-element block of a row, 512 lanes per workgroup), else SKINNY_ENOTSUP. Sums are fp32, one RNE rounding. M of any size runs in passes
  * of up to 4 rows (the kernel is meant for decode, M <= 4). Same conventions as above
  * otherwise (device pointers, asynchronous, no allocation).
  */

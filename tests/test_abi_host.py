@@ -154,7 +154,7 @@ def test_shard_argument_checks(L, ldr, ldy, M, flags, out_is_r, expect):
     ((A16, A16, A16, A16, 6, A16, A16, 1, 8, 64), 1),      # kbits above 5
     ((A16, A16, A16, A16, 4, A16, A16, -1, 8, 64), 1),     # negative M
     ((A16, A16, A16, A16, 4, A16, A16, 1, 8, 48), 3),      # K % 32 != 0
-    ((A16, A16, A16, A16, 4, A16, A16, 1, 8, 32 * 400), 3),  # K beyond the X staging limit
+    ((A16, A16, A16, A16, 4, A16, A16, 1, 8, 32 * 513), 3),  # K beyond one lane per block
     ((A16, A16, A16, None, 4, A16, A16, 1, 8, 64), 1),     # NULL codebook
     ((None, A16, A16, A16, 4, A16, A16, 1, 8, 64), 1),     # NULL X with K > 0
     ((A16, None, A16, A16, 4, A16, A16, 1, 8, 64), 1),     # NULL planes with K > 0

@@ -90,7 +90,7 @@ def test_kbit_x_zero_and_errors(sk):
     args = [d[0].data_ptr(), d[1].data_ptr(), d[2].data_ptr(), d[3].data_ptr()]
     assert L.skinny_kbit_gemv_bf16(*args, 6, d[4].data_ptr(), Y.data_ptr(), M, N, K, s) == 1      # kbits
     assert L.skinny_kbit_gemv_bf16(*args, 3, d[4].data_ptr(), Y.data_ptr(), M, N, K - 8, s) == 3  # K % 32
-    assert L.skinny_kbit_gemv_bf16(*args, 3, d[4].data_ptr(), Y.data_ptr(), M, N, 32 * 400, s) == 3  # K max
+    assert L.skinny_kbit_gemv_bf16(*args, 3, d[4].data_ptr(), Y.data_ptr(), M, N, 32 * 513, s) == 3  # K max
     assert L.skinny_kbit_gemv_bf16(d[0].data_ptr() + 2, *args[1:], 3, d[4].data_ptr(), Y.data_ptr(), M, N, K,
                                    s) == 2                                                        # X alignment
     with pytest.raises(ValueError):
