@@ -98,3 +98,47 @@ def make_kbit_inputs(M: int, N: int = N_DEFAULT, K: int = K_DEFAULT, kbits: int 
     inner = torch.rand((2 ** kbits - 2,), generator=g, dtype=torch.float32) * 2 - 1
     codebook = torch.cat([torch.tensor([-1.0]), inner.sort().values, torch.tensor([1.0])])
     return X, planes, scales, rs, codebook
+
+
+def make_kda_inputs(B: int, T: int = 4, H: int = 8, HV: int | None = None, K: int = 128, V: int = 128,
+                    ring_len: int = 16, seed: int = 0):
+    """Inputs of one KDA chain-verify step with the distributions of the sglang page
+    "benchmark/kernels/bench_kda_verify_sweep.py" (make_inputs): bf16 mixed ~ 0.5 N(0,1)
+    [B*T, 2HK + HV V], conv weight 0.3 N [dim, 4], conv bias 0.1 N [dim], conv_pool N
+    [B+1, 3, dim], a 0.5 N [B*T, HV K], b N [B*T, HV]; float32 A_log 0.5 N [HV],
+    dt_bias 0.5 N [HV K], ssm 0.2 N [B+1, HV, V, K]; outputs win_pool and inter_ssm zero;
+    ring buffers rawv [B+1, HV, R, V], rawk [B+1, H, R, K] (bf16), g [B+1, HV, R, K],
+    beta [B+1, HV, R] (float32) N(0,1); cache_indices = inter_indices = 0..B-1.
+    Drawn on the host from a seeded generator; returns a dict of CPU tensors."""
+    HV = H if HV is None else HV
+    g = torch.Generator().manual_seed(20260722 + 1000 * B + seed)
+    dim = 2 * H * K + HV * V
+    lines = slots = B + 1
+    rnd = lambda *s, dt=torch.bfloat16: torch.randn(*s, generator=g, dtype=torch.float32).to(dt)
+    return {
+        "mixed": (rnd(B * T, dim, dt=torch.float32) * 0.5).to(torch.bfloat16),
+        "w": (rnd(dim, 4, dt=torch.float32) * 0.3).to(torch.bfloat16),
+        "bias": (rnd(dim, dt=torch.float32) * 0.1).to(torch.bfloat16),
+        "a": (rnd(B * T, HV * K, dt=torch.float32) * 0.5).to(torch.bfloat16),
+        "b": rnd(B * T, HV),
+        "A_log": rnd(HV, dt=torch.float32) * 0.5,
+        "dt_bias": rnd(HV * K, dt=torch.float32) * 0.5,
+        "conv_pool": rnd(lines, 3, dim),
+        "ssm": rnd(slots, HV, V, K, dt=torch.float32) * 0.2,
+        "win_pool": torch.zeros(lines, T, 3, dim, dtype=torch.bfloat16),
+        "inter_ssm": torch.zeros(lines, T, HV, V, K, dtype=torch.float32),
+        "rawv": rnd(slots, HV, ring_len, V),
+        "rawk": rnd(slots, H, ring_len, K),
+        "g": rnd(slots, HV, ring_len, K, dt=torch.float32),
+        "beta": rnd(slots, HV, ring_len, dt=torch.float32),
+        "cache_indices": torch.arange(B, dtype=torch.int32),
+        "inter_indices": torch.arange(B, dtype=torch.int32),
+    }
+
+
+def kda_to_numpy(inp: dict) -> dict:
+    """The same tensors as numpy arrays, bf16 ones as uint16 bit patterns."""
+    out = {}
+    for k, t in inp.items():
+        out[k] = bits(t) if t.dtype == torch.bfloat16 else t.numpy().copy()
+    return out

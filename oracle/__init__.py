@@ -24,6 +24,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _KBIT_SRC = os.path.join(_HERE, "kbit.c")
+_KDA_SRC = os.path.join(_HERE, "kda.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _default = None
@@ -35,14 +36,15 @@ ROUND_PRODUCT = 1
 NO_NEG_ZERO = 2
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB, kbit_src: str = _KBIT_SRC) -> str:
-    """Compile oracle.c and kbit.c into one shared library (plain gcc: no fast-math, no FMA
-    contraction). A test may pass its own copy of either source."""
+def build(force: bool = True, src: str = _SRC, out: str = _LIB, kbit_src: str = _KBIT_SRC,
+          kda_src: str = _KDA_SRC) -> str:
+    """Compile oracle.c, kbit.c and kda.c into one shared library (plain gcc: no fast-math,
+    no FMA contraction). A test may pass its own copy of any source."""
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-           "-shared", "-pthread", src, kbit_src, "-o", tmp, "-lm"]
+           "-shared", "-pthread", src, kbit_src, kda_src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -98,8 +100,66 @@ class Oracle:
         lib.oracle_kbit_gemv_bf16.argtypes = [u16p, u32p, u8p, f32p, ctypes.c_int, u16p, u16p, f64p,
                                               i64, i64, i64]
         lib.oracle_kbit_gemv_bf16.restype = ctypes.c_int
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_kda_verify.argtypes = [i64] * 9 + [ctypes.c_double] + [u16p, u16p, u16p, u16p, i32p, i32p, u16p,
+                                                                         u16p, f32p, f32p, f32p, i32p, u16p, f64p,
+                                                                         u16p, u16p, f64p, f64p, u16p, f64p, f64p]
+        lib.oracle_kda_verify.restype = ctypes.c_int
         self.lib = lib
         self.path = path
+
+    # ---------------------------------------------------------------- KDA chain verify
+
+    def kda_verify(self, inp: dict, T: int, H: int, HV: int, K: int, V: int, scale: float,
+                   snapshots: bool = True, ring_len: int = 0) -> dict:
+        """One KDA verify step (kda.c) on the page's tensors, given as numpy arrays under the
+        page's names: bf16 bit patterns (uint16) for mixed [B*T, dim], w [dim, 4], bias [dim],
+        conv_pool [lines, 3, dim], a [B*T, HV*K], b [B*T, HV]; float32 A_log [HV],
+        dt_bias [HV*K], ssm [slots, HV, V, K]; int32 cache_indices and inter_indices [B].
+        Optional starting contents of the outputs: win_pool [lines, T, 3, dim] (uint16),
+        inter_ssm [lines, T, HV, V, K], rawv [slots, HV, R, V], rawk [slots, H, R, K]
+        (uint16), g [slots, HV, R, K], beta [slots, HV, R] (float64); absent ones start at 0.
+        Returns those outputs (snapshot ones if snapshots, ring ones if ring_len) plus o (bf16
+        bits [B*T, HV, V]), o_exact and conv_exact (float64, before their bf16 rounding)."""
+        c = lambda k, dt: np.ascontiguousarray(inp[k], dtype=dt)
+        mixed, w, bias, pool = (c(k, np.uint16) for k in ("mixed", "w", "bias", "conv_pool"))
+        a, b = c("a", np.uint16), c("b", np.uint16)
+        A_log, dt_bias, ssm = c("A_log", np.float32), c("dt_bias", np.float32), c("ssm", np.float32)
+        cidx, iidx = c("cache_indices", np.int32), c("inter_indices", np.int32)
+        B = cidx.shape[0]
+        dim = 2 * H * K + HV * V
+        lines, slots = pool.shape[0], ssm.shape[0]
+        if mixed.shape != (B * T, dim) or w.shape != (dim, 4) or pool.shape[1:] != (3, dim):
+            raise ValueError("bad conv shapes")
+        if ssm.shape[1:] != (HV, V, K) or a.shape != (B * T, HV * K) or b.shape != (B * T, HV):
+            raise ValueError("bad recurrence shapes")
+        def start(k, shape, dt):
+            if k in inp and inp[k] is not None:
+                return np.array(inp[k], dtype=dt, copy=True).reshape(shape)
+            return np.zeros(shape, dtype=dt)
+        res = {"win_pool": start("win_pool", (lines, T, 3, dim), np.uint16)}
+        if snapshots:
+            res["inter_ssm"] = start("inter_ssm", (lines, T, HV, V, K), np.float64)
+        if ring_len:
+            res["rawv"] = start("rawv", (slots, HV, ring_len, V), np.uint16)
+            res["rawk"] = start("rawk", (slots, H, ring_len, K), np.uint16)
+            res["g"] = start("g", (slots, HV, ring_len, K), np.float64)
+            res["beta"] = start("beta", (slots, HV, ring_len), np.float64)
+        res["o"] = np.zeros((B * T, HV, V), dtype=np.uint16)
+        res["o_exact"] = np.zeros((B * T, HV, V), dtype=np.float64)
+        res["conv_exact"] = np.zeros((B * T, dim), dtype=np.float64)
+        P = lambda k, ct: _ptr(res[k], ct) if k in res else None
+        u16, f64, f32, i32 = ctypes.c_uint16, ctypes.c_double, ctypes.c_float, ctypes.c_int32
+        rc = self.lib.oracle_kda_verify(B, T, H, HV, K, V, lines, slots, ring_len, float(scale),
+                                        _ptr(mixed, u16), _ptr(w, u16), _ptr(bias, u16), _ptr(pool, u16),
+                                        _ptr(cidx, i32), _ptr(iidx, i32), _ptr(a, u16), _ptr(b, u16),
+                                        _ptr(A_log, f32), _ptr(dt_bias, f32), _ptr(ssm, f32), _ptr(cidx, i32),
+                                        P("win_pool", u16), P("inter_ssm", f64), P("rawv", u16), P("rawk", u16),
+                                        P("g", f64), P("beta", f64), P("o", u16), P("o_exact", f64),
+                                        P("conv_exact", f64))
+        if rc != 0:
+            raise ValueError("oracle_kda_verify: bad arguments (%d)" % rc)
+        return res
 
     # ---------------------------------------------------------------- k-bit quantized GEMV
 
@@ -273,3 +333,8 @@ def kbit_dequant(planes, absmax, cb, k: int) -> np.ndarray:
 
 def kbit_gemv_bf16(X, planes, absmax, cb, k: int, R):
     return default().kbit_gemv_bf16(X, planes, absmax, cb, k, R)
+
+
+def kda_verify(inp: dict, T: int, H: int, HV: int, K: int, V: int, scale: float, snapshots: bool = True,
+               ring_len: int = 0) -> dict:
+    return default().kda_verify(inp, T, H, HV, K, V, scale, snapshots=snapshots, ring_len=ring_len)
