@@ -21,6 +21,9 @@ Other modes write JSONL rows (one per configuration or M) to --out:
                   N = 7168/--shards columns for rank --rank, R and Y as column blocks of the
                   full-width matrices, two roundings and no -0, W rotated over >= 40 copies
   --mode shard-sweep   the same over every built configuration
+  --mode kda      the KDA chain-verify step (sglang page "benchmark/kernels/bench_kda_verify_sweep.py"):
+                  H = HV = 8, K = V = 128, T = 4, B in --ms (default 1,4,16,64), snapshot and ring
+                  mode; states and outputs rotate over enough copies to exceed 320 MB
   --mode kbit     the k-bit quantized decode GEMV (bitsandbytes page "compare/main...QLORA-2.diff"),
                   N = 7168, K = 3584, k in --kbits, M in --ms (default 1,2,4); the planes and
                   scale bytes rotate over enough copies to exceed 308 MB
@@ -56,6 +59,21 @@ def kbit_algorithmic_bytes(M: int, N: int, K: int, kbits: int) -> int:
     """k bit-plane words and one scale byte per 32 weights read once, the 2^k-entry fp32
     codebook, X and R read once, Y written once (bf16)."""
     return N * (K // 32) * (4 * kbits + 1) + 4 * (1 << kbits) + 2 * M * K + 2 * M * N + 2 * M * N
+
+
+def kda_algorithmic_bytes(B: int, T: int, H: int, HV: int, K: int, V: int, ring: bool) -> int:
+    """Bytes one KDA verify call must move: the fp32 states read once; snapshots (T states
+    written) or ring entries (v, k bf16; g, beta fp32); the conv inputs (T tokens and 3 cached
+    inputs per channel, 4 taps and a bias) and windows (3 inputs per token); gates a, b,
+    dt_bias, A_log; the bf16 output."""
+    dim = 2 * H * K + HV * V
+    state = B * HV * V * K * 4
+    states_out = 0 if ring else T * state
+    ring_out = (B * HV * T * V * 2 + B * H * T * K * 2 + B * HV * T * K * 4 + B * HV * T * 4) if ring else 0
+    conv = B * T * dim * 2 + B * 3 * dim * 2 + dim * 5 * 2 + B * T * 3 * dim * 2
+    gates = B * T * HV * K * 2 + B * T * HV * 2 + HV * K * 4 + HV * 4
+    out = B * T * HV * V * 2
+    return state + states_out + ring_out + conv + gates + out
 
 
 def lookup_traffic(cfg: dict, M: int):
@@ -601,6 +619,76 @@ def run_kbit(args, sk):
         out.close()
 
 
+def run_kda(args, sk):
+    """The KDA verify step at the page's layer shape, per (B, mode): one JSON row with the mean
+    call time (graph replays of --calls launches rotating over copies of the states and
+    outputs), algorithmic GB/s and roofline fraction, and a sampled check against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from decode_skinny_addmm_amd import synth
+    T, H, HV, K, V = 4, 8, 8, 128, 128
+    Bs = [int(x) for x in args.ms.split(",")] if args.ms else [1, 4, 16, 64]
+    out = open(args.out, "a") if args.out else None
+    for B in Bs:
+        for ring in (False, True):
+            base = synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V)
+            per_copy = B * HV * V * K * 4 * (1 if ring else 1 + T)
+            copies = max(2, min(256, -(-320_000_000 // per_copy)))
+            shared = {k: v.cuda() for k, v in base.items() if k not in ("ssm", "inter_ssm", "rawv", "rawk", "g", "beta")}
+            per = []
+            for c in range(copies):
+                d = dict(shared)
+                d["ssm"] = base["ssm"].cuda()
+                if ring:
+                    for k in ("rawv", "rawk", "g", "beta"):
+                        d[k] = base[k].cuda()
+                else:
+                    d["inter_ssm"] = torch.empty_like(base["inter_ssm"], device="cuda")
+                per.append(d)
+            outs = [torch.empty((B * T, HV, V), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+            scale = K ** -0.5
+
+            class W:  # what time_graph expects: X, W[i], R[i], Y[i], copies
+                pass
+            wl = W()
+            wl.copies, wl.X, wl.W, wl.R, wl.Y = copies, None, per, [None] * copies, outs
+
+            def launch(X, Wc, R, Y):
+                return sk.kda_verify(Wc, T, H, HV, K, V, scale, snapshots=not ring, ring=ring, out=Y)
+            row = {"mode": "kda", "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V,
+                   "layout": "ring" if ring else "snapshots", "copies": copies, "calls": args.calls}
+            try:
+                per_us, total_ms = time_graph(launch, wl, args.calls, args.warmup, args.steps)
+                us = [p / args.calls for p in per_us]
+                mean_us = total_ms * 1000.0 / (args.steps * args.calls)
+                nbytes = kda_algorithmic_bytes(B, T, H, HV, K, V, ring)
+                row.update(summarize(us))
+                row.update({"mean_us_total": mean_us, "gbs": nbytes / (mean_us * 1e-6) / 1e9,
+                            "frac_hbm": nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nbytes})
+                # copy 0 against the oracle: output bits within 2 bf16 steps
+                o = launch(None, per[0], None, outs[0])
+                torch.cuda.synchronize()
+                ref = oracle.kda_verify(synth.kda_to_numpy(base), T, H, HV, K, V, scale, snapshots=not ring,
+                                        ring_len=16 if ring else 0)
+                g = synth.bits(o.cpu()).astype(np.int64)
+                r = ref["o"].astype(np.int64)
+                ordered = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+                row["o_within_2ulp_frac"] = float(np.mean(np.abs(ordered(g) - ordered(r)) <= 2))
+            except Exception as e:  # noqa: BLE001
+                row.update({"valid": False, "error": "%s: %s" % (type(e).__name__, e)})
+            line = json.dumps(row, sort_keys=True)
+            print(line, flush=True)
+            if out:
+                out.write(line + "\n")
+                out.flush()
+            del per, outs, shared
+            torch.cuda.empty_cache()
+    if out:
+        out.close()
+
+
 def synth_bits(t):
     from decode_skinny_addmm_amd import synth
     return synth.bits(t)
@@ -616,7 +704,7 @@ def main():
     p.add_argument("--calls", type=int, default=500, help="launches captured per graph (one step)")
     p.add_argument("--config", type=parse_config, default=None)
     p.add_argument("--mode", choices=("default", "sweep", "mcurve", "probe", "calib", "shard", "shard-sweep",
-                                        "kbit"),
+                                        "kbit", "kda"),
                    default="default")
     p.add_argument("--shards", type=int, default=8, help="shard/shard-sweep: ranks the 7168 columns split over")
     p.add_argument("--rank", type=int, default=3, help="shard/shard-sweep: which rank's column block")
@@ -653,6 +741,8 @@ def main():
         run_shard(args, sk)
     elif args.mode == "kbit":
         run_kbit(args, sk)
+    elif args.mode == "kda":
+        run_kda(args, sk)
     elif args.mode == "sweep":
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else [args.m or 16]
         paths = {int(x) for x in args.paths.split(",")} if args.paths else None

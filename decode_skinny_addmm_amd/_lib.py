@@ -22,7 +22,7 @@ CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
             "skinny_addmm_bf16_acc_f32", "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
-            "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32",
+            "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32", "skinny_kda_verify_bf16",
             "skinny_num_configs", "skinny_get_config",
             "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
             "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy")
@@ -38,6 +38,15 @@ class SkinnyConfig(ctypes.Structure):
 class SkinnyResources(ctypes.Structure):
     _fields_ = [("num_vgprs", ctypes.c_int32), ("spill_bytes", ctypes.c_int32),
                 ("lds_bytes_static", ctypes.c_int32), ("max_threads", ctypes.c_int32)]
+
+
+class SkinnyKdaArgs(ctypes.Structure):
+    """skinny_kda_args of include/skinny.h (pointers as integers, sizes, scale)."""
+    _fields_ = ([(f, ctypes.c_void_p) for f in ("mixed", "conv_w", "conv_b", "conv_pool", "cache_idx", "inter_idx",
+                                                "a", "b", "A_log", "dt_bias", "ssm", "conv_win", "snap", "ring_v",
+                                                "ring_k", "ring_g", "ring_beta", "out")]
+                + [(f, ctypes.c_int64) for f in ("B", "T", "H", "HV", "K", "V", "lines", "slots", "ring_len")]
+                + [("scale", ctypes.c_float)])
 
 
 class SkinnyError(RuntimeError):
@@ -78,6 +87,7 @@ def lib() -> ctypes.CDLL:
                                                   cfgp, vp]
     L.skinny_kbit_gemv_bf16.argtypes = [vp, vp, vp, vp, ctypes.c_int32, vp, vp, i64, i64, i64, vp]
     L.skinny_kbit_gemv_bf16_acc_f32.argtypes = [vp, vp, vp, vp, ctypes.c_int32, vp, vp, i64, i64, i64, vp]
+    L.skinny_kda_verify_bf16.argtypes = [ctypes.POINTER(SkinnyKdaArgs), vp]
     L.skinny_select_config.argtypes = [i64, i64, i64, cfgp]
     L.skinny_get_config.argtypes = [ctypes.c_int32, cfgp]
     L.skinny_config_resources.argtypes = [cfgp, ctypes.POINTER(SkinnyResources)]
@@ -91,7 +101,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, f).restype = ctypes.c_int
     for f in ("skinny_addmm_bf16", "skinny_addmm_bf16_with_config", "skinny_addmm_bf16_acc_f32",
               "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",
-              "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32",
+              "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32", "skinny_kda_verify_bf16",
               "skinny_select_config", "skinny_get_config", "skinny_config_resources",
               "skinny_num_configs", "skinny_last_hip_error"):
         getattr(L, f).restype = ctypes.c_int

@@ -158,10 +158,47 @@ skinny_status run_kbit(const void *X, const uint32_t *planes, const uint8_t *abs
     return SKINNY_OK;
 }
 
+skinny_status run_kda(const skinny_kda_args *a, void *stream) {
+    if (!a) return SKINNY_EINVAL;
+    if (a->B < 0 || a->T < 1 || a->H < 1 || a->HV < 1 || a->K < 1 || a->V < 1 || a->lines < 1 || a->slots < 1)
+        return SKINNY_EINVAL;
+    if (a->HV % a->H != 0) return SKINNY_EINVAL;
+    const bool ring_any = a->ring_v || a->ring_k || a->ring_g || a->ring_beta;
+    const bool ring_all = a->ring_v && a->ring_k && a->ring_g && a->ring_beta;
+    if (ring_any && !ring_all) return SKINNY_EINVAL;
+    if (ring_all && a->ring_len < a->T) return SKINNY_EINVAL;
+    if (a->K != 128 || a->V % 16 != 0 || a->T > 16) return SKINNY_ENOTSUP;
+    if (a->B > 65535 || a->HV > 65535 || a->V > 65535 * 16 || a->H * a->K + a->HV * a->V > INT_MAX / 2)
+        return SKINNY_ENOTSUP;
+    if (a->B == 0) return SKINNY_OK;
+    if (!a->mixed || !a->conv_w || !a->conv_b || !a->conv_pool || !a->cache_idx || !a->a || !a->b || !a->A_log ||
+        !a->dt_bias || !a->ssm || !a->out)
+        return SKINNY_EINVAL;
+    if ((a->conv_win || a->snap) && !a->inter_idx) return SKINNY_EINVAL;
+    const void *two[] = {a->mixed, a->conv_w, a->conv_b, a->conv_pool, a->a, a->b, a->out, a->conv_win,
+                         a->ring_v, a->ring_k};
+    for (const void *p : two)
+        if (p && !aligned(p, 2)) return SKINNY_EALIGN;
+    const void *four[] = {a->cache_idx, a->inter_idx, a->A_log, a->dt_bias, a->ring_g, a->ring_beta};
+    for (const void *p : four)
+        if (p && !aligned(p, 4)) return SKINNY_EALIGN;
+    if (!aligned(a->ssm, 16) || (a->snap && !aligned(a->snap, 16))) return SKINNY_EALIGN;
+    const hipError_t err = launch_kda_verify(*a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return SKINNY_EHIP;
+    }
+    return SKINNY_OK;
+}
+
 }  // namespace
 }  // namespace skinny
 
 extern "C" {
+
+skinny_status skinny_kda_verify_bf16(const skinny_kda_args *args, void *stream) {
+    return skinny::run_kda(args, stream);
+}
 
 skinny_status skinny_kbit_gemv_bf16(const void *X, const uint32_t *planes, const uint8_t *absmax,
                                     const float *codebook, int32_t kbits, const void *R, void *Y,

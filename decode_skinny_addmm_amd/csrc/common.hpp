@@ -65,6 +65,9 @@ struct KbitArgs {
 hipError_t launch_kbit_gemv(const KbitArgs &a);
 int64_t kbit_max_k();
 
+// One KDA chain-verify call (kda_verify.hip), validated by the C ABI layer.
+hipError_t launch_kda_verify(const skinny_kda_args &a, hipStream_t stream);
+
 // Registries filled by each kernel family's translation unit.
 const KernelEntry *gemv_entries(int *count);
 const KernelEntry *mfma_entries(int *count);

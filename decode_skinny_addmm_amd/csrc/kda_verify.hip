@@ -1,0 +1,253 @@
+// kda_verify.hip -- one layer of the KDA chain-verify step (conv1d update, KDA gate, gated delta
+// rule with per-token state snapshots or ring entries), fused into one kernel.
+//
+// Operation: the sglang page "benchmark/kernels/bench_kda_verify_sweep.py" (make_inputs and
+// make_runner: causal_conv1d_update then fused_sigmoid_gating_delta_rule_update with is_kda,
+// or fused_kda_conv_gating_verify), as defined in the C ABI header next to
+// skinny_kda_verify_bf16.
+//
+// Where the bytes are: per (batch row, value head) the fp32 state [V, K] is read once (64 KB
+// at V = K = 128) and, in snapshot mode, written T times; everything else (the conv inputs
+// of 2K + V channels, the gates) is a few KB. So the kernel is an HBM stream of states, and
+// the layout is chosen for it:
+//   * a workgroup owns BV rows of one state; 16 lanes per row, 8 consecutive K channels per
+//     lane: the state slice lives in registers for all T tokens, every load and snapshot store
+//     is a 16-byte vector and a row is 512 contiguous bytes;
+//   * the state load is issued first, so that its latency hides behind the conv and gate
+//     work; conv outputs (rounded to bf16, the precision the unfused path materialises),
+//     the normalised q and k, exp(g) and beta of all T tokens are staged in LDS once;
+//   * per token: decay, S k^ and S q^ as 8-wide partial dots closed by a 16-lane DPP sum;
+//   * the conv over q/k channels is recomputed by every workgroup of the head (256 channels
+//     x T tokens, a few hundred FMAs per lane) instead of a second kernel and a round trip;
+//     windows and ring entries shared by several workgroups are written by one of them.
+#include "common.hpp"
+
+namespace skinny {
+namespace {
+
+constexpr int KD = 128;        // head dimension of q and k (the page's shape)
+constexpr int TMAX = 16;       // most draft tokens per verify
+constexpr int CPL = KD / 16;   // K channels per lane
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // ror 8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // ror 4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // ror 2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // ror 1
+    return v;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Fast exp / log (the hardware exp2 and log2 with one scaling multiply, ~2 ulp): gate math
+// whose results are compared at 1e-5 relative, or that only feed fp32 state arithmetic.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
+
+// softplus with beta 1 and threshold 20; below -15 log1p(e^x) = e^x to fp32 precision
+__device__ __forceinline__ float softplus20(float x) {
+    return x > 20.0f ? x : (x < -15.0f ? fexp(x) : flog(1.0f + fexp(x)));
+}
+
+// grid (V / BV, HV, B), block GR * 16 lanes: GR groups of 16 lanes, each group owning RPG
+// consecutive state rows (BV = GR * RPG rows per workgroup).
+template <int GR, int RPG>
+__global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) {
+    constexpr int NT = GR * 16, BV = GR * RPG;
+    constexpr int GCH = (KD + NT - 1) / NT;   // gate channels per lane
+    __shared__ float sq[TMAX][KD], sk[TMAX][KD], seg[TMAX][KD];
+    __shared__ float sv[TMAX][BV];
+    __shared__ float sbeta[TMAX], sqn[TMAX], skn[TMAX];
+
+    const int tid = threadIdx.x;
+    const int v0 = blockIdx.x * BV, hv = blockIdx.y, b = blockIdx.z;
+    const int T = (int)a.T, H = (int)a.H, HV = (int)a.HV, V = (int)a.V, R = (int)a.ring_len;
+    const int group = HV / H, h = hv / group;
+    const size_t dim = (size_t)2 * H * KD + (size_t)HV * V;
+    const int cidx = a.cache_idx[b];
+    const int slot = clampi(cidx, 0, (int)a.slots - 1);
+    const int cline = clampi(cidx, 0, (int)a.lines - 1);
+    const int iline = (a.conv_win || a.snap) ? clampi(a.inter_idx[b], 0, (int)a.lines - 1) : 0;
+    const bool qk_writer = v0 == 0 && hv % group == 0;   // writes the q/k windows and ring k of head h
+    const bool head_writer = v0 == 0;                    // writes ring g and beta of value head hv
+    const bool ring = a.ring_v != nullptr;
+
+    // loads first, in the order they are used: the state slice (rows v0 + gi*RPG + r,
+    // channels 8j .. 8j+7), then this lane's gate inputs; the conv loop below loads its own
+    const int gi = tid >> 4, j = tid & 15;
+    float4 s4[RPG][2];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        const float *srow = a.ssm + (((size_t)slot * HV + hv) * V + v0 + gi * RPG + r) * KD + j * CPL;
+        s4[r][0] = *reinterpret_cast<const float4 *>(srow);
+        s4[r][1] = *reinterpret_cast<const float4 *>(srow + 4);
+    }
+    const uint16_t *ag = static_cast<const uint16_t *>(a.a);
+    const uint16_t *bg = static_cast<const uint16_t *>(a.b);
+    uint16_t araw[GCH][TMAX];
+    float dtb[GCH];
+#pragma unroll
+    for (int u = 0; u < GCH; ++u) {
+        const int c = min(tid + u * NT, KD - 1);
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+            araw[u][t] = t < T ? ag[((size_t)b * T + t) * HV * KD + (size_t)hv * KD + c] : (uint16_t)0;
+        dtb[u] = a.dt_bias[hv * KD + c];
+    }
+    const uint16_t braw = tid < T ? bg[((size_t)b * T + tid) * HV + hv] : (uint16_t)0;
+    const float negA = -fexp(a.A_log[hv]);
+
+    const uint16_t *mixed = static_cast<const uint16_t *>(a.mixed);
+    const uint16_t *cw = static_cast<const uint16_t *>(a.conv_w);
+    const uint16_t *cb = static_cast<const uint16_t *>(a.conv_b);
+    const uint16_t *pool = static_cast<const uint16_t *>(a.conv_pool);
+    uint16_t *win = static_cast<uint16_t *>(a.conv_win);
+
+    // conv over the q, k (head h) and v (rows v0 .. v0+BV of head hv) channels, one channel
+    // per lane at a time: all T outputs from the 3 cached and T new inputs
+    for (int i = tid; i < 2 * KD + BV; i += NT) {
+        const size_t ch = i < KD ? (size_t)h * KD + i
+                                 : i < 2 * KD ? (size_t)H * KD + (size_t)h * KD + (i - KD)
+                                              : (size_t)2 * H * KD + (size_t)hv * V + v0 + (i - 2 * KD);
+        float w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = bf16_bits_to_f32(cw[ch * 4 + q]);
+        const float bias = bf16_bits_to_f32(cb[ch]);
+        // loops run to TMAX with a guard, fully unrolled, so that seq stays in registers
+        uint16_t seq[TMAX + 3];
+#pragma unroll
+        for (int s = 0; s < 3; ++s) seq[s] = pool[((size_t)cline * 3 + s) * dim + ch];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) seq[3 + t] = t < T ? mixed[((size_t)b * T + t) * dim + ch] : (uint16_t)0;
+        const bool write_win = win && (i >= 2 * KD || qk_writer);
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t < T) {
+                float acc = bias;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = fmaf(w[q], bf16_bits_to_f32(seq[t + q]), acc);
+                // silu with the accurate exp and an IEEE division: this value is rounded to bf16
+                const uint16_t c = f32_to_bf16_rne(acc / (1.0f + expf(-acc)));
+                const float cf = bf16_bits_to_f32(c);
+                if (i < KD) {
+                    sq[t][i] = cf;
+                } else if (i < 2 * KD) {
+                    sk[t][i - KD] = cf;
+                    if (ring && qk_writer)
+                        static_cast<uint16_t *>(a.ring_k)[(((size_t)slot * H + h) * R + t) * KD + (i - KD)] = c;
+                } else {
+                    sv[t][i - 2 * KD] = cf;
+                    if (ring)
+                        static_cast<uint16_t *>(a.ring_v)[(((size_t)slot * HV + hv) * R + t) * V + v0 + (i - 2 * KD)] = c;
+                }
+                if (write_win)
+#pragma unroll
+                    for (int w2 = 0; w2 < 3; ++w2) win[(((size_t)iline * T + t) * 3 + w2) * dim + ch] = seq[t + 1 + w2];
+            }
+        }
+    }
+
+    // gates from the registers loaded above: exp(g) per token and K channel, beta per token
+#pragma unroll
+    for (int u = 0; u < GCH; ++u) {
+        const int c = tid + u * NT;
+        if (c < KD) {
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {
+                    const float g = negA * softplus20(bf16_bits_to_f32(araw[u][t]) + dtb[u]);
+                    seg[t][c] = fexp(g);
+                    if (ring && head_writer) a.ring_g[(((size_t)slot * HV + hv) * R + t) * KD + c] = g;
+                }
+            }
+        }
+    }
+    if (tid < T) {
+        const float beta = 1.0f / (1.0f + fexp(-bf16_bits_to_f32(braw)));
+        sbeta[tid] = beta;
+        if (ring && head_writer) a.ring_beta[((size_t)slot * HV + hv) * R + tid] = beta;
+    }
+    __syncthreads();
+
+    // L2 norms of q and k per token: one 16-lane group per (token, q|k)
+    for (int r = gi; r < 2 * T; r += GR) {
+        const float *src = r < T ? &sq[r][j * CPL] : &sk[r - T][j * CPL];
+        float p = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) p = fmaf(src[c], src[c], p);
+        p = row16_sum(p);
+        if (j == 0) {
+            const float n = 1.0f / sqrtf(p + 1e-6f);
+            if (r < T) sqn[r] = n * a.scale;
+            else skn[r - T] = n;
+        }
+    }
+    __syncthreads();
+
+    float S[RPG][CPL];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        S[r][0] = s4[r][0].x; S[r][1] = s4[r][0].y; S[r][2] = s4[r][0].z; S[r][3] = s4[r][0].w;
+        S[r][4] = s4[r][1].x; S[r][5] = s4[r][1].y; S[r][6] = s4[r][1].z; S[r][7] = s4[r][1].w;
+    }
+    uint16_t *out = static_cast<uint16_t *>(a.out);
+    for (int t = 0; t < T; ++t) {
+        const float qn = sqn[t], kn = skn[t], beta = sbeta[t];
+        float e[CPL], kk[CPL], qq[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            e[c] = seg[t][j * CPL + c];
+            kk[c] = sk[t][j * CPL + c] * kn;
+            qq[c] = sq[t][j * CPL + c] * qn;
+        }
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+            const int vl = gi * RPG + r;            // row within the workgroup
+            float skp = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                S[r][c] *= e[c];
+                skp = fmaf(S[r][c], kk[c], skp);
+            }
+            skp = row16_sum(skp);
+            const float u = beta * (sv[t][vl] - skp);
+            float op = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                S[r][c] = fmaf(u, kk[c], S[r][c]);
+                op = fmaf(S[r][c], qq[c], op);
+            }
+            op = row16_sum(op);
+            if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op);
+            if (a.snap) {
+                float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
+                *reinterpret_cast<float4 *>(dst) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+                *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[r][4], S[r][5], S[r][6], S[r][7]);
+            }
+        }
+    }
+}
+
+template <int GR, int RPG>
+hipError_t launch_shape(const skinny_kda_args &a, hipStream_t stream) {
+    constexpr int BV = GR * RPG;
+    dim3 grid((unsigned)(a.V / BV), (unsigned)a.HV, (unsigned)a.B);
+    hipLaunchKernelGGL((kda_verify_kernel<GR, RPG>), grid, dim3(GR * 16), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kda_verify(const skinny_kda_args &a, hipStream_t stream) {
+    // Rows per workgroup: the conv of the q/k channels and the gates are recomputed by every
+    // workgroup of a (batch row, value head), so take the most rows that still leave >= 512
+    // workgroups (2 per CU); small batches fall back to 16 and then 4 rows per workgroup.
+    const int64_t rows = a.B * a.HV * a.V;
+    if (a.V % 128 == 0 && rows / 128 >= 512) return launch_shape<16, 8>(a, stream);
+    if (a.V % 64 == 0 && rows / 64 >= 512) return launch_shape<16, 4>(a, stream);
+    if (a.V % 32 == 0 && rows / 32 >= 512) return launch_shape<16, 2>(a, stream);
+    if (rows / 16 >= 256) return launch_shape<16, 1>(a, stream);
+    return launch_shape<4, 1>(a, stream);
+}
+
+}  // namespace skinny

@@ -11,7 +11,7 @@ import ctypes
 
 import torch
 
-from ._lib import (CONFIG_FIELDS, FLAG_NO_NEG_ZERO, FLAG_ROUND_PRODUCT, SkinnyConfig, SkinnyError,  # noqa: F401
+from ._lib import (CONFIG_FIELDS, FLAG_NO_NEG_ZERO, FLAG_ROUND_PRODUCT, SkinnyConfig, SkinnyError, SkinnyKdaArgs,  # noqa: F401
                    SkinnyResources, check, lib)
 
 
@@ -219,6 +219,57 @@ def kbit_gemv_acc_f32(X, planes, absmax, codebook, kbits: int, R, out=None, stre
                                                  codebook.data_ptr(), int(kbits), R.data_ptr(), out.data_ptr(),
                                                  M, N, K, _stream_ptr(stream, X.device))
     check(st, "skinny_kbit_gemv_bf16_acc_f32")
+    return out
+
+
+def kda_verify(inp: dict, T: int, H: int, HV: int, K: int, V: int, scale: float, snapshots: bool = True,
+               ring: bool = False, out=None, stream=None) -> torch.Tensor:
+    """One KDA chain-verify step (skinny_kda_verify_bf16) on device tensors named as on the
+    sglang benchmark page: bf16 mixed [B*T, dim], w [dim, 4], bias [dim], conv_pool
+    [lines, 3, dim], win_pool [lines, T, 3, dim], a [B*T, HV*K], b [B*T, HV]; float32 A_log
+    [HV], dt_bias [HV*K], ssm [slots, HV, V, K], inter_ssm [lines, T, HV, V, K], ring
+    buffers rawv [slots, HV, R, V], rawk [slots, H, R, K] (bf16), g [slots, HV, R, K], beta
+    [slots, HV, R] (float32); int32 cache_indices, inter_indices [B]. Writes win_pool, and
+    inter_ssm (snapshots) or the ring buffers (ring); returns o bf16 [B*T, HV, V]."""
+    dim = 2 * H * K + HV * V
+    B = int(inp["cache_indices"].shape[0])
+    spec = {"mixed": (torch.bfloat16, (B * T, dim)), "w": (torch.bfloat16, (dim, 4)),
+            "bias": (torch.bfloat16, (dim,)), "a": (torch.bfloat16, (B * T, HV * K)),
+            "b": (torch.bfloat16, (B * T, HV)), "A_log": (torch.float32, (HV,)),
+            "dt_bias": (torch.float32, (HV * K,)), "cache_indices": (torch.int32, (B,)),
+            "inter_indices": (torch.int32, (B,))}
+    lines = int(inp["conv_pool"].shape[0])
+    slots = int(inp["ssm"].shape[0])
+    spec["conv_pool"] = (torch.bfloat16, (lines, 3, dim))
+    spec["win_pool"] = (torch.bfloat16, (lines, T, 3, dim))
+    spec["ssm"] = (torch.float32, (slots, HV, V, K))
+    R = 0
+    if snapshots:
+        spec["inter_ssm"] = (torch.float32, (lines, T, HV, V, K))
+    if ring:
+        R = int(inp["rawv"].shape[2])
+        spec.update({"rawv": (torch.bfloat16, (slots, HV, R, V)), "rawk": (torch.bfloat16, (slots, H, R, K)),
+                     "g": (torch.float32, (slots, HV, R, K)), "beta": (torch.float32, (slots, HV, R))})
+    for name, (dt, shape) in spec.items():
+        t = inp.get(name)
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if t.dtype != dt or tuple(t.shape) != shape:
+            raise ValueError("%s must be %s %s, got %s %s" % (name, dt, shape, t.dtype, tuple(t.shape)))
+    if out is None:
+        out = torch.empty((B * T, HV, V), dtype=torch.bfloat16, device=inp["mixed"].device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B * T, HV, V) or not out.is_contiguous():
+        raise ValueError("out must be contiguous bf16 [B*T, HV, V]")
+    p = lambda name: inp[name].data_ptr() if name in spec else None
+    args = SkinnyKdaArgs(mixed=p("mixed"), conv_w=p("w"), conv_b=p("bias"), conv_pool=p("conv_pool"),
+                         cache_idx=p("cache_indices"), inter_idx=p("inter_indices"), a=p("a"), b=p("b"),
+                         A_log=p("A_log"), dt_bias=p("dt_bias"), ssm=p("ssm"), conv_win=p("win_pool"),
+                         snap=p("inter_ssm"), ring_v=p("rawv"), ring_k=p("rawk"), ring_g=p("g"),
+                         ring_beta=p("beta"), out=out.data_ptr(), B=B, T=T, H=H, HV=HV, K=K, V=V,
+                         lines=lines, slots=slots, ring_len=R, scale=float(scale))
+    with torch.cuda.device(inp["mixed"].device):
+        st = lib().skinny_kda_verify_bf16(ctypes.byref(args), _stream_ptr(stream, inp["mixed"].device))
+    check(st, "skinny_kda_verify_bf16")
     return out
 
 

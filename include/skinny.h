@@ -199,6 +199,61 @@ SKINNY_API skinny_status skinny_kbit_gemv_bf16_acc_f32(const void *X, const uint
                                                        int32_t kbits, const void *R, float *ACC,
                                                        int64_t M, int64_t N, int64_t K, void *stream);
 
+/*
+ * One layer of the KDA chain-verify step of speculative decoding (the sglang page
+ * "benchmark/kernels/bench_kda_verify_sweep.py": its make_inputs gives the tensors below, its
+ * make_runner the calls; the unfused leg is causal_conv1d_update followed by
+ * fused_sigmoid_gating_delta_rule_update with is_kda, the fused legs are
+ * fused_kda_conv_gating_verify). For batch row b (T draft tokens), per channel d of the
+ * mixed q|k|v projection and per value head hv:
+ *
+ *   conv:  c[t, d] = bf16( silu( bias[d] + sum_w conv_w[d, w] * seq_d[t + w] ) ),
+ *          seq_d = conv_pool[cache_idx[b], 0..2, d] then mixed[b*T + 0..T-1, d];
+ *          q = c[:, h*K ..], k = c[:, H*K + h*K ..], v = c[:, 2*H*K + hv*V ..], h = hv / (HV/H)
+ *   gate:  g[t, c] = -exp(A_log[hv]) * softplus(a[b*T+t, hv*K + c] + dt_bias[hv*K + c])
+ *          (softplus with beta 1, threshold 20); beta_t = sigmoid(b[b*T+t, hv])
+ *   norm:  q^ = scale * q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)
+ *   state: S = ssm[cache_idx[b], hv] ([V, K] fp32); per token t:
+ *          S *= exp(g[t]) per K channel; u = beta_t (v_t - S k^); S += u k^T; o_t = S q^
+ *   outputs: out[b*T + t, hv, :] = bf16(o_t);
+ *          conv_win[inter_idx[b], t, w, d] = seq_d[t + 1 + w] (w = 0..2), when non-NULL;
+ *          snapshot mode (snap non-NULL): snap[inter_idx[b], t, hv] = S after token t;
+ *          ring mode (ring pointers non-NULL), position t of slot cache_idx[b]:
+ *          ring_v[., hv, t, :] = v_t, ring_k[., h, t, :] = k_t (bf16 conv outputs, before the
+ *          norm), ring_g[., hv, t, :] = g[t], ring_beta[., hv, t] = beta_t.
+ *   ssm and conv_pool are read only (the verify step commits no state).
+ * Which of these readings are the page's and which are taken where it is silent is listed
+ * with the oracle that defines them (oracle/kda.c).
+ *
+ * Layouts (row-major, device pointers, all bf16 unless noted):
+ *   mixed [B*T, dim], dim = 2*H*K + HV*V;  conv_w [dim, 4];  conv_b [dim];
+ *   conv_pool [lines, 3, dim];  conv_win [lines, T, 3, dim];
+ *   a [B*T, HV*K];  b [B*T, HV];  A_log float [HV];  dt_bias float [HV*K];
+ *   ssm float [slots, HV, V, K];  snap float [lines, T, HV, V, K];
+ *   ring_v [slots, HV, ring_len, V];  ring_k [slots, H, ring_len, K];
+ *   ring_g float [slots, HV, ring_len, K];  ring_beta float [slots, HV, ring_len];
+ *   cache_idx, inter_idx int32 [B] (values outside 0..slots-1 / 0..lines-1 are clamped);
+ *   out [B*T, HV, V].
+ * Supported: K == 128, V a multiple of 16, 1 <= T <= 16, HV a multiple of H, ring_len >= T
+ * when the ring is used (else SKINNY_ENOTSUP / SKINNY_EINVAL). ssm and snap must be 16-byte
+ * aligned. B == 0 is a no-op. Asynchronous on `stream`, no allocation, capturable.
+ */
+typedef struct skinny_kda_args {
+    const void *mixed, *conv_w, *conv_b, *conv_pool;
+    const int32_t *cache_idx, *inter_idx;
+    const void *a, *b;
+    const float *A_log, *dt_bias, *ssm;
+    void *conv_win;                 /* may be NULL */
+    float *snap;                    /* may be NULL */
+    void *ring_v, *ring_k;          /* ring mode: all four non-NULL, or all four NULL */
+    float *ring_g, *ring_beta;
+    void *out;
+    int64_t B, T, H, HV, K, V, lines, slots, ring_len;
+    float scale;
+} skinny_kda_args;
+
+SKINNY_API skinny_status skinny_kda_verify_bf16(const skinny_kda_args *args, void *stream);
+
 /* Number of configurations built into the library, and the i-th of them (0-based). */
 SKINNY_API int32_t skinny_num_configs(void);
 SKINNY_API skinny_status skinny_get_config(int32_t index, skinny_config *out);

@@ -169,3 +169,36 @@ def test_kbit_argument_checks(L, args, expect):
     assert L.skinny_kbit_gemv_bf16(*args, None) == expect
     if args[6] is not None:
         assert L.skinny_kbit_gemv_bf16_acc_f32(*args, None) == expect
+
+
+def _kda_args(**over):
+    base = dict(mixed=A16, conv_w=A16, conv_b=A16, conv_pool=A16, cache_idx=A16, inter_idx=A16, a=A16, b=A16,
+                A_log=A16, dt_bias=A16, ssm=A16, conv_win=A16, snap=A16, ring_v=None, ring_k=None, ring_g=None,
+                ring_beta=None, out=A16, B=2, T=4, H=1, HV=1, K=128, V=16, lines=3, slots=3, ring_len=0,
+                scale=0.088)
+    base.update(over)
+    return _lib.SkinnyKdaArgs(**base)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(K=64), 3),                                   # head dimension other than 128
+    (dict(T=17), 3),                                   # more than 16 draft tokens
+    (dict(V=8), 3),                                    # V not a multiple of 16
+    (dict(T=0), 1),                                    # no tokens
+    (dict(H=2, HV=3), 1),                              # value heads not a multiple of q/k heads
+    (dict(ring_v=A16), 1),                             # ring buffers given in part
+    (dict(ring_v=A16, ring_k=A16, ring_g=A16, ring_beta=A16, ring_len=2), 1),   # ring shorter than T
+    (dict(mixed=None), 1),                             # missing input
+    (dict(inter_idx=None), 1),                         # windows/snapshots without their index
+    (dict(ssm=A16 + 4), 2),                            # state not 16-byte aligned
+    (dict(snap=A16 + 8), 2),                           # snapshots not 16-byte aligned
+    (dict(mixed=A2 + 1), 2),                           # bf16 input at an odd address
+    (dict(B=0, mixed=None, ssm=None), 0),              # empty batch: no-op
+])
+def test_kda_argument_checks(L, over, expect):
+    args = _kda_args(**over)
+    assert L.skinny_kda_verify_bf16(ctypes.byref(args), None) == expect
+
+
+def test_kda_null_args(L):
+    assert L.skinny_kda_verify_bf16(None, None) == 1

@@ -95,3 +95,25 @@ def test_kbit_x_zero_and_errors(sk):
                                    s) == 2                                                        # X alignment
     with pytest.raises(ValueError):
         sk.kbit_gemv(d[0], d[1], d[2], d[3], 4, d[4])                                             # shape of planes
+
+
+def test_kbit_k_zero_is_residual(sk):
+    M, N = 3, 40
+    R = torch.randn(M, N).to(torch.bfloat16).cuda()
+    X = torch.empty((M, 0), dtype=torch.bfloat16, device="cuda")
+    planes = torch.empty((N, 0, 4), dtype=torch.int32, device="cuda")
+    amax = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    cb = torch.linspace(-1, 1, 16, dtype=torch.float32, device="cuda")
+    Y = sk.kbit_gemv(X, planes, amax, cb, 4, R)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.cpu().view(torch.int16), R.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K", [(2, 16384), (1, 14336), (4, 8192)])
+def test_kbit_long_rows(sk, M, K):
+    """Long rows: one lane per block up to 512 blocks, a row group of one row per workgroup."""
+    X, ps, As, rs, cb = synth.make_kbit_inputs(M, 48, K, kbits=3, seed=K)
+    Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, 3, rs[0])
+    Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), 3, synth.bits(rs[0]))
+    P.check_y(Yg, Yo, Ao, "kbit long K=%d" % K)
+    P.check_acc(Ag, Ao, "kbit long K=%d" % K)

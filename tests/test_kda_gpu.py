@@ -1,0 +1,155 @@
+"""GPU parity of the KDA chain-verify step (skinny_kda_verify_bf16) against the CPU oracle
+(oracle/kda.c), in snapshot and ring mode.
+
+Bars (the kernel computes in fp32 after the bf16 conv outputs, the oracle in fp64):
+  * conv windows: bit-exact (data movement);
+  * ring k and v (the bf16 conv outputs): at most 1 bf16 step, and equal wherever the exact
+    conv value is more than 1e-6 from a rounding midpoint (fp32 and fp64 sums may round a
+    value that close either way);
+  * ring g and beta: relative 1e-5;
+  * o: the dense path's rule, 2 bf16 ULP where |o| >= 2^-12, else 2^-18 absolute;
+  * snapshots: |S - S_exact| <= 1e-5 |S_exact| + 5e-4 rms(S_exact) (fp32 state arithmetic is
+    ~1e-6 relative; a k value rounded the other way moves the state by ~5e-6). A state row
+    whose value input v, at that token or an earlier one, lies within 1e-6 of a bf16 rounding
+    midpoint (the oracle's fp64 conv value; the kernel's fp32 one may round the other way) may
+    move by one bf16 step of v times beta times |k^|: that row gets 2^-8 max|v| max|k^| more.
+    A wrong decay, beta or head mapping moves states by 1e-2 or more.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+from decode_skinny_addmm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_skinny_addmm_amd as d
+    d.ops.lib()
+    return d
+
+
+def midpoint_distance(x):
+    """Distance of each float64 value to the nearest bf16 rounding midpoint."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    m, e = np.frexp(x)
+    scaled = m * 256.0                       # bf16 steps at 1.0 in these units
+    frac = scaled - np.floor(scaled)
+    return np.abs(frac - 0.5) * np.ldexp(1.0 / 256.0, e)
+
+
+def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True):
+    t_inp = synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V, seed=seed)
+    if permute:
+        lines = B + 1
+        t_inp["cache_indices"] = torch.tensor([lines - 1 - i for i in range(B)], dtype=torch.int32)
+        t_inp["inter_indices"] = torch.tensor([(i + 1) % lines for i in range(B)], dtype=torch.int32)
+    n_inp = synth.kda_to_numpy(t_inp)
+    scale = K ** -0.5
+    print("kda", dict(B=B, T=T, H=H, HV=HV, K=K, V=V, ring=ring, seed=seed), flush=True)
+    d = {k: v.cuda() for k, v in t_inp.items()}
+    o = sk.kda_verify(d, T, H, HV, K, V, scale, snapshots=not ring, ring=ring)
+    torch.cuda.synchronize()
+    ref = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=not ring, ring_len=16 if ring else 0)
+    what = "kda B=%d T=%d H=%d HV=%d V=%d ring=%s" % (B, T, H, HV, V, ring)
+    assert np.array_equal(synth.bits(d["win_pool"].cpu()), ref["win_pool"]), what + ": windows"
+    P.check_y(P.bits_of(o), ref["o"], ref["o_exact"], what + ": o")
+    dim = 2 * H * K + HV * V
+    conv_bits = oracle.round_bf16(ref["conv_exact"])
+    near = midpoint_distance(ref["conv_exact"]) < 1e-6
+    if ring:
+        for name in ("rawv", "rawk"):
+            g = synth.bits(d[name].cpu()).astype(np.int64)
+            r = ref[name].astype(np.int64)
+            diff = np.abs(P.ordered(g) - P.ordered(r))
+            assert diff.max() <= 1, what + ": " + name
+            assert (diff > 0).sum() <= int(near.sum()), what + ": %s differs away from a midpoint" % name
+        assert np.allclose(d["g"].cpu().numpy(), ref["g"], rtol=1e-5, atol=1e-7), what + ": g"
+        assert np.allclose(d["beta"].cpu().numpy(), ref["beta"], rtol=1e-5, atol=1e-7), what + ": beta"
+    else:
+        S = d["inter_ssm"].cpu().numpy().astype(np.float64)
+        Se = ref["inter_ssm"]
+        rms = float(np.sqrt(np.mean(Se ** 2)))
+        err = np.abs(S - Se)
+        lim = 1e-5 * np.abs(Se) + 5e-4 * rms
+        # rows (line, t, hv, v) whose v input at a token <= t is near a midpoint
+        vnear = near[:, 2 * H * K:].reshape(B, T, HV, V)
+        vnear = np.cumsum(vnear, axis=1) > 0                       # at this token or before
+        conv = oracle.bf16_bits_to_f64(conv_bits)
+        vmax = float(np.abs(conv[:, 2 * H * K:]).max())
+        khat_max = 0.0
+        for row in range(B * T):
+            for h in range(H):
+                k = conv[row, H * K + h * K:H * K + (h + 1) * K]
+                khat_max = max(khat_max, float(np.abs(k).max() / np.sqrt(k @ k + 1e-6)))
+        extra = 2.0 ** -8 * vmax * khat_max
+        lines = np.array([int(i) for i in n_inp["inter_indices"]])
+        for bi in range(B):
+            lim[lines[bi]] += np.where(vnear[bi][:, :, :, None], extra, 0.0)
+        bad = err > lim
+        assert not bad.any(), what + ": %d snapshot values off, max err %g (rms %g, %d rows near a midpoint)" % (
+            int(bad.sum()), err.max(), rms, int(vnear.sum()))
+    assert conv_bits.shape == (B * T, dim)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+@pytest.mark.parametrize("B,T,H,HV,V", [(1, 4, 1, 1, 16), (3, 4, 2, 4, 32), (2, 1, 1, 2, 16), (2, 16, 1, 1, 16),
+                                        (5, 3, 2, 2, 48)])
+def test_kda_small(sk, B, T, H, HV, V, ring):
+    run_case(sk, B, T, H, HV, 128, V, ring)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_kda_page_shape(sk, B, ring):
+    """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens; B = 16 launches 16 rows per
+    workgroup, B = 4 eight, B = 1 four."""
+    run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
+
+
+def test_kda_gqa_page(sk):
+    run_case(sk, 2, 4, 8, 16, 128, 128, False)
+
+
+def test_kda_ring_bitwise_between_launch_shapes(sk):
+    """The page's guard compares the ring bytes of two implementations; here the same inputs
+    run through launches with different rows per workgroup (B = 1 uses four rows, the same
+    batch row inside B = 64 uses sixteen) must fill identical ring bytes for that row."""
+    T, H, HV, K, V = 4, 8, 8, 128, 128
+    big = synth.make_kda_inputs(64, T=T, H=H, HV=HV, K=K, V=V, seed=3)
+    db = {k: v.cuda() for k, v in big.items()}
+    sk.kda_verify(db, T, H, HV, K, V, K ** -0.5, snapshots=False, ring=True)
+    one = {}
+    for k, v in big.items():
+        if k in ("mixed", "a", "b"):
+            one[k] = v[:T].clone()
+        elif k in ("cache_indices", "inter_indices"):
+            one[k] = v[:1].clone()
+        elif k in ("w", "bias", "A_log", "dt_bias"):
+            one[k] = v.clone()
+        else:
+            one[k] = v[:2].clone()      # lines/slots 0 and 1
+    d1 = {k: v.cuda() for k, v in one.items()}
+    d1["rawv"].zero_(); d1["rawk"].zero_(); d1["g"].zero_(); d1["beta"].zero_()
+    sk.kda_verify(d1, T, H, HV, K, V, K ** -0.5, snapshots=False, ring=True)
+    torch.cuda.synchronize()
+    for name in ("rawv", "rawk", "g", "beta"):
+        a = db[name][0, :, :T].cpu()
+        b = d1[name][0, :, :T].cpu()
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), name
+
+
+def test_kda_argument_errors(sk):
+    T, H, HV, K, V = 4, 1, 1, 128, 16
+    d = {k: v.cuda() for k, v in synth.make_kda_inputs(2, T=T, H=H, HV=HV, K=K, V=V).items()}
+    with pytest.raises(ValueError):
+        sk.kda_verify(d, T, H, HV, K, 32, K ** -0.5)          # V does not match the tensors
+    with pytest.raises(ValueError):
+        sk.kda_verify(d, T + 1, H, HV, K, V, K ** -0.5)       # T does not match the tensors
