@@ -26,7 +26,7 @@ namespace skinny {
 namespace {
 
 constexpr int KD = 128;        // head dimension of q and k (the page's shape)
-constexpr int TMAX = 16;       // most draft tokens per verify
+constexpr int TLIM = 16;       // most draft tokens per verify
 constexpr int CPL = KD / 16;   // K channels per lane
 
 __device__ __forceinline__ float row16_sum(float v) {
@@ -51,7 +51,9 @@ __device__ __forceinline__ float softplus20(float x) {
 
 // grid (V / BV, HV, B), block GR * 16 lanes: GR groups of 16 lanes, each group owning RPG
 // consecutive state rows (BV = GR * RPG rows per workgroup).
-template <int GR, int RPG>
+// TMAX: token bound of this instance (4, 8 or 16 >= T): token loops unroll to it, token loads
+// past T repeat token T - 1 (unconditional loads keep the memory waits exact).
+template <int GR, int RPG, int TMAX>
 __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) {
     constexpr int NT = GR * 16, BV = GR * RPG;
     constexpr int GCH = (KD + NT - 1) / NT;   // gate channels per lane
@@ -72,15 +74,34 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
     const bool head_writer = v0 == 0;                    // writes ring g and beta of value head hv
     const bool ring = a.ring_v != nullptr;
 
-    // loads first, in the order they are used: the state slice (rows v0 + gi*RPG + r,
-    // channels 8j .. 8j+7), then this lane's gate inputs; the conv loop below loads its own
+    // Loads, all issued before the first wait and in the order they are used (the memory
+    // counter is waited on in issue order): this lane's conv inputs, its gate inputs, then the
+    // state rows (the largest part, needed last: its transfer overlaps the conv, the gates and
+    // the first rows of the recurrence).
+    constexpr int NCH = 2 * KD + BV;             // conv channels of this workgroup
+    constexpr int CCH = (NCH + NT - 1) / NT;     // ... per lane
     const int gi = tid >> 4, j = tid & 15;
-    float4 s4[RPG][2];
+    const uint16_t *mixed = static_cast<const uint16_t *>(a.mixed);
+    const uint16_t *cw = static_cast<const uint16_t *>(a.conv_w);
+    const uint16_t *cb = static_cast<const uint16_t *>(a.conv_b);
+    const uint16_t *pool = static_cast<const uint16_t *>(a.conv_pool);
+    uint16_t *win = static_cast<uint16_t *>(a.conv_win);
+    size_t chs[CCH];
+    uint16_t wraw[CCH][4], braw_c[CCH], seq[CCH][TMAX + 3];   // fully unrolled: registers
 #pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-        const float *srow = a.ssm + (((size_t)slot * HV + hv) * V + v0 + gi * RPG + r) * KD + j * CPL;
-        s4[r][0] = *reinterpret_cast<const float4 *>(srow);
-        s4[r][1] = *reinterpret_cast<const float4 *>(srow + 4);
+    for (int u = 0; u < CCH; ++u) {
+        const int i = min(tid + u * NT, NCH - 1);
+        const size_t ch = i < KD ? (size_t)h * KD + i
+                                 : i < 2 * KD ? (size_t)H * KD + (size_t)h * KD + (i - KD)
+                                              : (size_t)2 * H * KD + (size_t)hv * V + v0 + (i - 2 * KD);
+        chs[u] = ch;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wraw[u][q] = cw[ch * 4 + q];
+        braw_c[u] = cb[ch];
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) seq[u][s2] = pool[((size_t)cline * 3 + s2) * dim + ch];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) seq[u][3 + t] = mixed[((size_t)b * T + min(t, T - 1)) * dim + ch];
     }
     const uint16_t *ag = static_cast<const uint16_t *>(a.a);
     const uint16_t *bg = static_cast<const uint16_t *>(a.b);
@@ -91,58 +112,58 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
         const int c = min(tid + u * NT, KD - 1);
 #pragma unroll
         for (int t = 0; t < TMAX; ++t)
-            araw[u][t] = t < T ? ag[((size_t)b * T + t) * HV * KD + (size_t)hv * KD + c] : (uint16_t)0;
+            araw[u][t] = ag[((size_t)b * T + min(t, T - 1)) * HV * KD + (size_t)hv * KD + c];
         dtb[u] = a.dt_bias[hv * KD + c];
     }
-    const uint16_t braw = tid < T ? bg[((size_t)b * T + tid) * HV + hv] : (uint16_t)0;
-    const float negA = -fexp(a.A_log[hv]);
+    const uint16_t braw = bg[((size_t)b * T + min(tid, T - 1)) * HV + hv];
+    const float alog = a.A_log[hv];
+    asm volatile("" ::: "memory");             // the state loads stay after the inputs above
+    float4 s4[RPG][2];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        const float *srow = a.ssm + (((size_t)slot * HV + hv) * V + v0 + gi * RPG + r) * KD + j * CPL;
+        s4[r][0] = *reinterpret_cast<const float4 *>(srow);
+        s4[r][1] = *reinterpret_cast<const float4 *>(srow + 4);
+    }
+    const float negA = -fexp(alog);
 
-    const uint16_t *mixed = static_cast<const uint16_t *>(a.mixed);
-    const uint16_t *cw = static_cast<const uint16_t *>(a.conv_w);
-    const uint16_t *cb = static_cast<const uint16_t *>(a.conv_b);
-    const uint16_t *pool = static_cast<const uint16_t *>(a.conv_pool);
-    uint16_t *win = static_cast<uint16_t *>(a.conv_win);
-
-    // conv over the q, k (head h) and v (rows v0 .. v0+BV of head hv) channels, one channel
-    // per lane at a time: all T outputs from the 3 cached and T new inputs
-    for (int i = tid; i < 2 * KD + BV; i += NT) {
-        const size_t ch = i < KD ? (size_t)h * KD + i
-                                 : i < 2 * KD ? (size_t)H * KD + (size_t)h * KD + (i - KD)
-                                              : (size_t)2 * H * KD + (size_t)hv * V + v0 + (i - 2 * KD);
-        float w[4];
+    // conv over the q, k (head h) and v (rows v0 .. v0+BV of head hv) channels: all T outputs
+    // of a channel from its 3 cached and T new inputs
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = bf16_bits_to_f32(cw[ch * 4 + q]);
-        const float bias = bf16_bits_to_f32(cb[ch]);
-        // loops run to TMAX with a guard, fully unrolled, so that seq stays in registers
-        uint16_t seq[TMAX + 3];
+    for (int u = 0; u < CCH; ++u) {
+        const int i = tid + u * NT;
+        if (i < NCH) {
+            const size_t ch = chs[u];
+            float w[4];
 #pragma unroll
-        for (int s = 0; s < 3; ++s) seq[s] = pool[((size_t)cline * 3 + s) * dim + ch];
+            for (int q = 0; q < 4; ++q) w[q] = bf16_bits_to_f32(wraw[u][q]);
+            const float bias = bf16_bits_to_f32(braw_c[u]);
+            const bool write_win = win && (i >= 2 * KD || qk_writer);
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) seq[3 + t] = t < T ? mixed[((size_t)b * T + t) * dim + ch] : (uint16_t)0;
-        const bool write_win = win && (i >= 2 * KD || qk_writer);
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {
+                    float acc = bias;
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                float acc = bias;
+                    for (int q = 0; q < 4; ++q) acc = fmaf(w[q], bf16_bits_to_f32(seq[u][t + q]), acc);
+                    // silu with the accurate exp and an IEEE division: this value is rounded to bf16
+                    const uint16_t c = f32_to_bf16_rne(acc / (1.0f + expf(-acc)));
+                    const float cf = bf16_bits_to_f32(c);
+                    if (i < KD) {
+                        sq[t][i] = cf;
+                    } else if (i < 2 * KD) {
+                        sk[t][i - KD] = cf;
+                        if (ring && qk_writer)
+                            static_cast<uint16_t *>(a.ring_k)[(((size_t)slot * H + h) * R + t) * KD + (i - KD)] = c;
+                    } else {
+                        sv[t][i - 2 * KD] = cf;
+                        if (ring)
+                            static_cast<uint16_t *>(a.ring_v)[(((size_t)slot * HV + hv) * R + t) * V + v0 + (i - 2 * KD)] = c;
+                    }
+                    if (write_win)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc = fmaf(w[q], bf16_bits_to_f32(seq[t + q]), acc);
-                // silu with the accurate exp and an IEEE division: this value is rounded to bf16
-                const uint16_t c = f32_to_bf16_rne(acc / (1.0f + expf(-acc)));
-                const float cf = bf16_bits_to_f32(c);
-                if (i < KD) {
-                    sq[t][i] = cf;
-                } else if (i < 2 * KD) {
-                    sk[t][i - KD] = cf;
-                    if (ring && qk_writer)
-                        static_cast<uint16_t *>(a.ring_k)[(((size_t)slot * H + h) * R + t) * KD + (i - KD)] = c;
-                } else {
-                    sv[t][i - 2 * KD] = cf;
-                    if (ring)
-                        static_cast<uint16_t *>(a.ring_v)[(((size_t)slot * HV + hv) * R + t) * V + v0 + (i - 2 * KD)] = c;
+                        for (int w2 = 0; w2 < 3; ++w2)
+                            win[(((size_t)iline * T + t) * 3 + w2) * dim + ch] = seq[u][t + 1 + w2];
                 }
-                if (write_win)
-#pragma unroll
-                    for (int w2 = 0; w2 < 3; ++w2) win[(((size_t)iline * T + t) * 3 + w2) * dim + ch] = seq[t + 1 + w2];
             }
         }
     }
@@ -184,45 +205,110 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
     }
     __syncthreads();
 
-    float S[RPG][CPL];
-#pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-        S[r][0] = s4[r][0].x; S[r][1] = s4[r][0].y; S[r][2] = s4[r][0].z; S[r][3] = s4[r][0].w;
-        S[r][4] = s4[r][1].x; S[r][5] = s4[r][1].y; S[r][6] = s4[r][1].z; S[r][7] = s4[r][1].w;
-    }
+    // the recurrence, row by row (all T tokens of a row before the next): each row waits only
+    // for its own 512 bytes of state, so the state stream overlaps the arithmetic
     uint16_t *out = static_cast<uint16_t *>(a.out);
-    for (int t = 0; t < T; ++t) {
-        const float qn = sqn[t], kn = skn[t], beta = sbeta[t];
-        float e[CPL], kk[CPL], qq[CPL];
+    if constexpr (TMAX == 4) {
+        // up to 4 tokens: this lane's exp(g), k^ and q^ slices of every token, beta and the v
+        // values of its rows move to registers once; the row pairs below then run on VALU and
+        // DPP alone
+        float e[4][CPL], kk[4][CPL], qq[4][CPL], bt[4], vv[4][RPG];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            e[c] = seg[t][j * CPL + c];
-            kk[c] = sk[t][j * CPL + c] * kn;
-            qq[c] = sq[t][j * CPL + c] * qn;
+        for (int t = 0; t < 4; ++t) {
+            const int tc = min(t, T - 1);
+            const float kn = skn[tc], qn = sqn[tc];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                e[t][c] = seg[tc][j * CPL + c];
+                kk[t][c] = sk[tc][j * CPL + c] * kn;
+                qq[t][c] = sq[tc][j * CPL + c] * qn;
+            }
+            bt[t] = sbeta[tc];
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) vv[t][r] = sv[tc][gi * RPG + r];
         }
+        constexpr int RP = RPG >= 2 ? 2 : 1;   // rows per step of the loop
+#pragma unroll
+        for (int r0 = 0; r0 < RPG; r0 += RP) {
+            float S[RP][CPL];
+#pragma unroll
+            for (int x = 0; x < RP; ++x) {
+                S[x][0] = s4[r0 + x][0].x; S[x][1] = s4[r0 + x][0].y; S[x][2] = s4[r0 + x][0].z;
+                S[x][3] = s4[r0 + x][0].w; S[x][4] = s4[r0 + x][1].x; S[x][5] = s4[r0 + x][1].y;
+                S[x][6] = s4[r0 + x][1].z; S[x][7] = s4[r0 + x][1].w;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (t < T) {
+                    float skp[RP], op[RP];
+#pragma unroll
+                    for (int x = 0; x < RP; ++x) {
+                        skp[x] = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            S[x][c] *= e[t][c];
+                            skp[x] = fmaf(S[x][c], kk[t][c], skp[x]);
+                        }
+                    }
+#pragma unroll
+                    for (int x = 0; x < RP; ++x) skp[x] = row16_sum(skp[x]);
+#pragma unroll
+                    for (int x = 0; x < RP; ++x) {
+                        const float u = bt[t] * (vv[t][r0 + x] - skp[x]);
+                        op[x] = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            S[x][c] = fmaf(u, kk[t][c], S[x][c]);
+                            op[x] = fmaf(S[x][c], qq[t][c], op[x]);
+                        }
+                    }
+#pragma unroll
+                    for (int x = 0; x < RP; ++x) op[x] = row16_sum(op[x]);
+#pragma unroll
+                    for (int x = 0; x < RP; ++x) {
+                        const int vl = gi * RPG + r0 + x;
+                        if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op[x]);
+                        if (a.snap) {
+                            float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
+                            *reinterpret_cast<float4 *>(dst) = make_float4(S[x][0], S[x][1], S[x][2], S[x][3]);
+                            *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[x][4], S[x][5], S[x][6], S[x][7]);
+                        }
+                    }
+                }
+            }
+        }
+    } else {
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             const int vl = gi * RPG + r;            // row within the workgroup
-            float skp = 0.0f;
+            float S[CPL] = {s4[r][0].x, s4[r][0].y, s4[r][0].z, s4[r][0].w,
+                            s4[r][1].x, s4[r][1].y, s4[r][1].z, s4[r][1].w};
+            for (int t = 0; t < T; ++t) {
+                const float kn = skn[t];
+                float skp = 0.0f;
+                float kk[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                S[r][c] *= e[c];
-                skp = fmaf(S[r][c], kk[c], skp);
-            }
-            skp = row16_sum(skp);
-            const float u = beta * (sv[t][vl] - skp);
-            float op = 0.0f;
+                for (int c = 0; c < CPL; ++c) {
+                    kk[c] = sk[t][j * CPL + c] * kn;
+                    S[c] *= seg[t][j * CPL + c];
+                    skp = fmaf(S[c], kk[c], skp);
+                }
+                skp = row16_sum(skp);
+                const float u = sbeta[t] * (sv[t][vl] - skp);
+                const float qn = sqn[t];
+                float op = 0.0f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                S[r][c] = fmaf(u, kk[c], S[r][c]);
-                op = fmaf(S[r][c], qq[c], op);
-            }
-            op = row16_sum(op);
-            if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op);
-            if (a.snap) {
-                float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
-                *reinterpret_cast<float4 *>(dst) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
-                *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[r][4], S[r][5], S[r][6], S[r][7]);
+                for (int c = 0; c < CPL; ++c) {
+                    S[c] = fmaf(u, kk[c], S[c]);
+                    op = fmaf(S[c], sq[t][j * CPL + c] * qn, op);
+                }
+                op = row16_sum(op);
+                if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op);
+                if (a.snap) {
+                    float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
+                    *reinterpret_cast<float4 *>(dst) = make_float4(S[0], S[1], S[2], S[3]);
+                    *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[4], S[5], S[6], S[7]);
+                }
             }
         }
     }
@@ -232,7 +318,12 @@ template <int GR, int RPG>
 hipError_t launch_shape(const skinny_kda_args &a, hipStream_t stream) {
     constexpr int BV = GR * RPG;
     dim3 grid((unsigned)(a.V / BV), (unsigned)a.HV, (unsigned)a.B);
-    hipLaunchKernelGGL((kda_verify_kernel<GR, RPG>), grid, dim3(GR * 16), 0, stream, a);
+    if (a.T <= 4)
+        hipLaunchKernelGGL((kda_verify_kernel<GR, RPG, 4>), grid, dim3(GR * 16), 0, stream, a);
+    else if (a.T <= 8)
+        hipLaunchKernelGGL((kda_verify_kernel<GR, RPG, 8>), grid, dim3(GR * 16), 0, stream, a);
+    else
+        hipLaunchKernelGGL((kda_verify_kernel<GR, RPG, TLIM>), grid, dim3(GR * 16), 0, stream, a);
     return hipGetLastError();
 }
 
