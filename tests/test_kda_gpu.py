@@ -9,11 +9,14 @@ Bars (the kernel computes in fp32 after the bf16 conv outputs, the oracle in fp6
   * ring g and beta: relative 1e-5;
   * o: the dense path's rule, 2 bf16 ULP where |o| >= 2^-12, else 2^-18 absolute;
   * snapshots: |S - S_exact| <= 1e-5 |S_exact| + 5e-4 rms(S_exact) (fp32 state arithmetic is
-    ~1e-6 relative; a k value rounded the other way moves the state by ~5e-6). A state row
+    ~1e-6 relative). A state row
     whose value input v, at that token or an earlier one, lies within 1e-6 of a bf16 rounding
     midpoint (the oracle's fp64 conv value; the kernel's fp32 one may round the other way) may
     move by one bf16 step of v times beta times |k^|: that row gets 2^-8 max|v| max|k^| more.
-    A wrong decay, beta or head mapping moves states by 1e-2 or more.
+    Likewise a key value k_c near a midpoint moves column c of the head's states by u dk^_c,
+    |u| <= max|v| + sqrt(K) max|S|, dk^_c <= 2^-7 max|k^|: that column, from that token on,
+    gets 2^-7 max|k^| (max|v| + sqrt(K) max|S|) more. A wrong decay, beta or head mapping moves
+    every state by 1e-2 or more.
 """
 import numpy as np
 import pytest
@@ -90,26 +93,34 @@ def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True):
                 khat_max = max(khat_max, float(np.abs(k).max() / np.sqrt(k @ k + 1e-6)))
         extra = 2.0 ** -8 * vmax * khat_max
         lines = np.array([int(i) for i in n_inp["inter_indices"]])
+        knear = near[:, H * K:2 * H * K].reshape(B, T, H, K)
+        knear = np.cumsum(knear, axis=1) > 0
+        extra_k = 2.0 ** -7 * khat_max * (vmax + np.sqrt(K) * float(np.abs(Se).max()))
+        group = HV // H
         for bi in range(B):
             lim[lines[bi]] += np.where(vnear[bi][:, :, :, None], extra, 0.0)
+            kcols = np.repeat(knear[bi], group, axis=1)            # [T, HV, K]
+            lim[lines[bi]] += np.where(kcols[:, :, None, :], extra_k, 0.0)
         bad = err > lim
-        assert not bad.any(), what + ": %d snapshot values off, max err %g (rms %g, %d rows near a midpoint)" % (
-            int(bad.sum()), err.max(), rms, int(vnear.sum()))
+        msg = ": %d snapshot values off, max err %g (rms %g, %d rows and %d columns near a midpoint)" % (
+            int(bad.sum()), err.max(), rms, int(vnear.sum()), int(knear.sum()))
+        assert not bad.any(), what + msg
     assert conv_bits.shape == (B * T, dim)
 
 
 @pytest.mark.parametrize("ring", [False, True])
 @pytest.mark.parametrize("B,T,H,HV,V", [(1, 4, 1, 1, 16), (3, 4, 2, 4, 32), (2, 1, 1, 2, 16), (2, 16, 1, 1, 16),
-                                        (5, 3, 2, 2, 48)])
+                                        (5, 3, 2, 2, 48), (2, 6, 1, 2, 32), (3, 8, 2, 2, 16), (1, 11, 1, 1, 16)])
 def test_kda_small(sk, B, T, H, HV, V, ring):
     run_case(sk, B, T, H, HV, 128, V, ring)
 
 
 @pytest.mark.parametrize("ring", [False, True])
-@pytest.mark.parametrize("B", [1, 4, 16])
+@pytest.mark.parametrize("B", [1, 4, 16, 32])
 def test_kda_page_shape(sk, B, ring):
-    """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens; B = 16 launches 16 rows per
-    workgroup, B = 4 eight, B = 1 four."""
+    """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens. The launch takes 4 state rows
+    per workgroup at B = 1, 16 at B = 4, 32 at B = 16 and 64 at B = 32 (128 at B = 64, in the
+    ring test below)."""
     run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
 
 
