@@ -721,7 +721,7 @@ def main():
                    help="mcurve: add torch.addmm (the vendor library) as a context row")
     args = p.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: this library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
