@@ -118,9 +118,9 @@ def test_kda_small(sk, B, T, H, HV, V, ring):
 @pytest.mark.parametrize("ring", [False, True])
 @pytest.mark.parametrize("B", [1, 4, 16, 32])
 def test_kda_page_shape(sk, B, ring):
-    """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens. The launch takes 4 state rows
-    per workgroup at B = 1, 16 at B = 4, 32 at B = 16 and 64 at B = 32 (128 at B = 64, in the
-    ring test below)."""
+    """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens. The launch takes 16 state rows
+    per workgroup at B = 1 and 4, 32 at B = 16 and 64 at B = 32 (128 at B = 64, in the ring test
+    below)."""
     run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
 
 
@@ -130,8 +130,8 @@ def test_kda_gqa_page(sk):
 
 def test_kda_ring_bitwise_between_launch_shapes(sk):
     """The page's guard compares the ring bytes of two implementations; here the same inputs
-    run through launches with different rows per workgroup (B = 1 uses four rows, the same
-    batch row inside B = 64 uses sixteen) must fill identical ring bytes for that row."""
+    run through launches with different rows per workgroup (B = 1 uses 16 rows, the same batch
+    row inside B = 64 uses 128) must fill identical ring bytes for that row."""
     T, H, HV, K, V = 4, 8, 8, 128, 128
     big = synth.make_kda_inputs(64, T=T, H=H, HV=HV, K=K, V=V, seed=3)
     db = {k: v.cuda() for k, v in big.items()}
