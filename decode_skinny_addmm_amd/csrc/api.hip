@@ -168,7 +168,8 @@ skinny_status run_kda(const skinny_kda_args *a, void *stream) {
     if (ring_any && !ring_all) return SKINNY_EINVAL;
     if (ring_all && a->ring_len < a->T) return SKINNY_EINVAL;
     if (a->K != 128 || a->V % 16 != 0 || a->T > 16) return SKINNY_ENOTSUP;
-    if (a->B > 65535 || a->HV > 65535 || a->V > 65535 * 16 || a->H * a->K + a->HV * a->V > INT_MAX / 2)
+    if (a->B > 65535 || a->HV > 65535 || a->V > 65535 * 16 || a->H * a->K + a->HV * a->V > INT_MAX / 2 ||
+        a->lines > INT_MAX || a->slots > INT_MAX || a->ring_len > INT_MAX)
         return SKINNY_ENOTSUP;
     if (a->B == 0) return SKINNY_OK;
     if (!a->mixed || !a->conv_w || !a->conv_b || !a->conv_pool || !a->cache_idx || !a->a || !a->b || !a->A_log ||

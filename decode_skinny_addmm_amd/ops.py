@@ -250,16 +250,20 @@ def kda_verify(inp: dict, T: int, H: int, HV: int, K: int, V: int, scale: float,
         R = int(inp["rawv"].shape[2])
         spec.update({"rawv": (torch.bfloat16, (slots, HV, R, V)), "rawk": (torch.bfloat16, (slots, H, R, K)),
                      "g": (torch.float32, (slots, HV, R, K)), "beta": (torch.float32, (slots, HV, R))})
+    dev = inp["mixed"].device if isinstance(inp.get("mixed"), torch.Tensor) else None
     for name, (dt, shape) in spec.items():
         t = inp.get(name)
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
             raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if t.device != dev:
+            raise ValueError("%s is on %s, mixed on %s: all tensors must be on one GPU" % (name, t.device, dev))
         if t.dtype != dt or tuple(t.shape) != shape:
             raise ValueError("%s must be %s %s, got %s %s" % (name, dt, shape, t.dtype, tuple(t.shape)))
     if out is None:
         out = torch.empty((B * T, HV, V), dtype=torch.bfloat16, device=inp["mixed"].device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B * T, HV, V) or not out.is_contiguous():
-        raise ValueError("out must be contiguous bf16 [B*T, HV, V]")
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (B * T, HV, V) or not out.is_contiguous()
+          or out.device != dev):
+        raise ValueError("out must be contiguous bf16 [B*T, HV, V] on the inputs' GPU")
     p = lambda name: inp[name].data_ptr() if name in spec else None
     args = SkinnyKdaArgs(mixed=p("mixed"), conv_w=p("w"), conv_b=p("bias"), conv_pool=p("conv_pool"),
                          cache_idx=p("cache_indices"), inter_idx=p("inter_indices"), a=p("a"), b=p("b"),

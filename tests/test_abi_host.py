@@ -202,3 +202,8 @@ def test_kda_argument_checks(L, over, expect):
 
 def test_kda_null_args(L):
     assert L.skinny_kda_verify_bf16(None, None) == 1
+
+
+def test_kda_sizes_beyond_int_range(L):
+    args = _kda_args(lines=2 ** 31)
+    assert L.skinny_kda_verify_bf16(ctypes.byref(args), None) == 3
