@@ -227,7 +227,7 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
 #pragma unroll
             for (int r = 0; r < RPG; ++r) vv[t][r] = sv[tc][gi * RPG + r];
         }
-        constexpr int RP = RPG >= 2 ? 2 : 1;   // rows per step of the loop
+        constexpr int RP = RPG >= 4 ? 4 : RPG;   // rows per step of the loop (independent chains)
 #pragma unroll
         for (int r0 = 0; r0 < RPG; r0 += RP) {
             float S[RP][CPL];
