@@ -117,3 +117,16 @@ def test_kbit_long_rows(sk, M, K):
     Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), 3, synth.bits(rs[0]))
     P.check_y(Yg, Yo, Ao, "kbit long K=%d" % K)
     P.check_acc(Ag, Ao, "kbit long K=%d" % K)
+
+
+def test_kbit_poisoned_output_fully_written(sk):
+    """Every output is written: Y starts as NaN (bf16 and fp32 entry) and must hold none after."""
+    for M, N, K in ((1, 300, 512), (4, 1000, 3584), (3, 77, 1024)):
+        X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=3, seed=M)
+        d = [t.cuda() for t in (X, ps[0], As[0], cb, rs[0])]
+        Y = torch.full_like(d[4], float("nan"))
+        sk.kbit_gemv(d[0], d[1], d[2], d[3], 3, d[4], out=Y)
+        A = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        sk.kbit_gemv_acc_f32(d[0], d[1], d[2], d[3], 3, d[4], out=A)
+        torch.cuda.synchronize()
+        assert not torch.isnan(Y.float()).any() and not torch.isnan(A).any(), (M, N, K)

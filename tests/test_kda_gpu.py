@@ -164,3 +164,34 @@ def test_kda_argument_errors(sk):
         sk.kda_verify(d, T, H, HV, K, 32, K ** -0.5)          # V does not match the tensors
     with pytest.raises(ValueError):
         sk.kda_verify(d, T + 1, H, HV, K, V, K ** -0.5)       # T does not match the tensors
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_kda_poisoned_outputs_fully_written(sk, ring):
+    """o, the windows of the batch rows' lines and their snapshots (or ring positions < T) start
+    as NaN and must hold none after the call; lines and slots of no batch row stay NaN."""
+    B, T, H, HV, K, V = 3, 4, 2, 4, 128, 32
+    d = {k: v.cuda() for k, v in synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V).items()}
+    d["cache_indices"] = torch.tensor([3, 0, 2], dtype=torch.int32, device="cuda")
+    d["inter_indices"] = torch.tensor([1, 3, 0], dtype=torch.int32, device="cuda")
+    nan = float("nan")
+    d["win_pool"].fill_(nan)
+    d["inter_ssm"].fill_(nan)
+    for k in ("rawv", "rawk", "g", "beta"):
+        d[k].fill_(nan)
+    out = torch.full((B * T, HV, V), nan, dtype=torch.bfloat16, device="cuda")
+    sk.kda_verify(d, T, H, HV, K, V, K ** -0.5, snapshots=not ring, ring=ring, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    lines = [1, 3, 0]
+    assert not torch.isnan(d["win_pool"][lines].float()).any()
+    assert torch.isnan(d["win_pool"][2].float()).all()
+    if ring:
+        for k in ("rawv", "rawk", "g", "beta"):
+            t = d[k][[3, 0, 2]][:, :, :T].float()
+            assert not torch.isnan(t).any(), k
+            assert torch.isnan(d[k][[3, 0, 2]][:, :, T:].float()).all(), k
+            assert torch.isnan(d[k][1].float()).all(), k
+    else:
+        assert not torch.isnan(d["inter_ssm"][lines]).any()
+        assert torch.isnan(d["inter_ssm"][2]).all()
