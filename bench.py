@@ -459,6 +459,7 @@ def run_default(args, sk):
                      "bytes_per_launch": algorithmic_bytes(M),
                      "mfma_frac": round(flops / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "device": torch.cuda.get_device_name(0),
+        "device_meta": device_meta(),
     }
     if not args.no_reference:
         ref = reference_rows(sk, wl, args.calls, max(2, args.warmup // 4), max(5, args.steps // 5))
@@ -474,14 +475,44 @@ def run_default(args, sk):
     print(json.dumps(row), flush=True)
 
 
+def device_meta() -> dict:
+    """What the rows are measured on: device name, gfx architecture, CU count, HIP and torch
+    versions, and the host's usable cores (the CPU oracle's baseline runs there)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"device": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "cus": p.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cores": len(os.sched_getaffinity(0))}
+
+
+def done_rows(path):
+    """(m, n, k, config) of the valid rows already in a JSONL file: a sweep given the same --out
+    with --resume skips them, so an interrupted sweep continues where it stopped."""
+    keys = set()
+    if path and os.path.exists(path):
+        for line in open(path):
+            try:
+                r = json.loads(line)
+            except ValueError:
+                continue
+            if r.get("valid", True) and "config" in r and "m" in r:
+                keys.add((r["m"], r.get("n"), r.get("k"), json.dumps(r["config"], sort_keys=True)))
+    return keys
+
+
 def sweep_rows(args, sk, Ms, config_lists):
     import torch
     from decode_skinny_addmm_amd._lib import PATH_SIMT
+    done = done_rows(args.out) if getattr(args, "resume", False) else set()
     out = open(args.out, "a") if args.out else None
-    meta = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip}
+    meta = device_meta()
     for M in Ms:
+        todo = [c for c in config_lists(M)
+                if (M, args.n, args.k, json.dumps(c, sort_keys=True)) not in done]
+        if not todo:
+            continue
         wl = Workload(M, args.copies, args.n, args.k)
-        for cfg in config_lists(M):
+        for cfg in todo:
             row = {"m": M, "n": wl.N, "k": wl.K, "config": cfg, "copies": args.copies,
                    "calls": args.calls, **meta}
             if cfg.get("path") == PATH_SIMT:
@@ -710,6 +741,8 @@ def main():
     p.add_argument("--rank", type=int, default=3, help="shard/shard-sweep: which rank's column block")
     p.add_argument("--kbits", type=str, default="2,3,4,5", help="kbit: comma-separated bits per weight")
     p.add_argument("--out", type=str, default=None)
+    p.add_argument("--resume", action="store_true",
+                   help="sweep/mcurve: skip the (M, N, K, config) rows already valid in --out")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")

@@ -1,0 +1,49 @@
+"""Host-side pieces of bench.py (CPU only): byte counts, sweep resume, the one-GPU guard."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_dense_algorithmic_bytes():
+    # W once, X once, R read, Y written (bf16): 51 380 224 + 35 840 M at N = 7168, K = 3584
+    for M in (1, 4, 16, 256):
+        assert bench.algorithmic_bytes(M) == 51380224 + 35840 * M
+
+
+def test_kbit_algorithmic_bytes():
+    # k plane words and one scale byte per 32 weights, the codebook, X, R, Y
+    assert bench.kbit_algorithmic_bytes(1, 7168, 3584, 4) == 7168 * 112 * 17 + 64 + 2 * 3584 + 4 * 7168
+    assert bench.kbit_algorithmic_bytes(2, 64, 64, 2) == 64 * 2 * 9 + 16 + 2 * 2 * 64 + 4 * 2 * 64
+
+
+def test_kda_algorithmic_bytes():
+    B, T, H, HV, K, V = 2, 4, 1, 1, 128, 16
+    dim = 2 * H * K + HV * V
+    base = B * T * dim * 2 + B * 3 * dim * 2 + dim * 5 * 2 + B * T * 3 * dim * 2 \
+        + B * T * HV * K * 2 + B * T * HV * 2 + HV * K * 4 + HV * 4 + B * T * HV * V * 2
+    state = B * HV * V * K * 4
+    assert bench.kda_algorithmic_bytes(B, T, H, HV, K, V, False) == base + state * (1 + T)
+    ring = B * HV * T * V * 2 + B * H * T * K * 2 + B * HV * T * K * 4 + B * HV * T * 4
+    assert bench.kda_algorithmic_bytes(B, T, H, HV, K, V, True) == base + state + ring
+
+
+def test_done_rows_skips_valid_rows_only(tmp_path):
+    f = tmp_path / "rows.jsonl"
+    rows = [{"m": 4, "n": 7168, "k": 3584, "config": {"path": 0, "block_size": 448}},
+            {"m": 8, "n": 7168, "k": 3584, "config": {"path": 1}, "valid": False}]
+    f.write_text("\n".join(json.dumps(r) for r in rows) + "\nnot json\n")
+    done = bench.done_rows(str(f))
+    assert done == {(4, 7168, 3584, json.dumps({"block_size": 448, "path": 0}, sort_keys=True))}
+    assert bench.done_rows(str(tmp_path / "missing.jsonl")) == set()
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2 and "one GPU only" in p.stderr
