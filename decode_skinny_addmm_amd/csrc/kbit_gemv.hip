@@ -220,8 +220,15 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float *pr = part + (size_t)grp * MT * BPR + m * BPR;
+            // up to 8 partials per lane in one batch of independent LDS reads (BPR <= 128),
+            // then a loop for longer rows
+            float part8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) part8[u] = pr[min(s16 + 16 * u, BPR - 1)];
             float v = 0.0f;
-            for (int b = s16; b < BPR; b += 16) v += pr[b];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v += s16 + 16 * u < BPR ? part8[u] : 0.0f;
+            for (int b = s16 + 128; b < BPR; b += 16) v += pr[b];
             v = row16_sum(v);
             if (s16 == 0 && wn < N && m0 + m < M) store_output<ACC>(out, Epilogue{N, N, 0u}, m0 + m, wn, v, bf16_bits_to_f32(rbits[m]));
         }
