@@ -27,6 +27,31 @@ def _as_config(cfg) -> SkinnyConfig | None:
     return SkinnyConfig(*vals)
 
 
+def _byte_span(t: torch.Tensor) -> tuple[int, int]:
+    """[first, last) byte addresses of a tensor with non-negative strides."""
+    if t.numel() == 0:
+        return t.data_ptr(), t.data_ptr()
+    last = sum((n - 1) * st for n, st in zip(t.shape, t.stride()))
+    return t.data_ptr(), t.data_ptr() + (last + 1) * t.element_size()
+
+
+def _overlaps(a: torch.Tensor, b: torch.Tensor) -> bool:
+    (a0, a1), (b0, b1) = _byte_span(a), _byte_span(b)
+    return a0 < b1 and b0 < a1
+
+
+def _check_aliasing(inputs, R, out):
+    """The output may be R itself (same address, strides and dtype: every residual is read
+    before its own output is written) but must not overlap the other inputs or any other
+    part of R. Overlap is judged on byte spans, so two column blocks interleaved in one wide
+    matrix count as overlapping (a conservative refusal, never a missed overlap)."""
+    if any(_overlaps(out, t) for t in inputs):
+        raise ValueError("out must not overlap the operands other than R")
+    if _overlaps(out, R) and not (out.data_ptr() == R.data_ptr() and out.stride() == R.stride()
+                                  and out.dtype == R.dtype):
+        raise ValueError("out may be R itself but must not partially overlap it")
+
+
 def _check_operands(X, W, R, out, out_dtype):
     for name, t in (("X", X), ("W", W), ("R", R), ("out", out)):
         if not isinstance(t, torch.Tensor):
@@ -51,6 +76,7 @@ def _check_operands(X, W, R, out, out_dtype):
     devs = {t.device for t in (X, W, R, out)}
     if len(devs) != 1:
         raise ValueError("all operands must be on the same device")
+    _check_aliasing((X, W), R, out)
     return M, N, K
 
 
@@ -129,6 +155,7 @@ def _check_shard_operands(X, W, R, out, out_dtype):
             raise ValueError("%s row stride must be >= N" % name)
     if len({t.device for t in (X, W, R, out)}) != 1:
         raise ValueError("all operands must be on the same device")
+    _check_aliasing((X, W), R, out)
     return M, N, K, (R.stride(0) if M > 1 else N), (out.stride(0) if M > 1 else N)
 
 
@@ -193,6 +220,7 @@ def _check_kbit(X, planes, absmax, codebook, kbits, R, out, out_dtype):
         raise ValueError("codebook must have 2^kbits entries")
     if tuple(R.shape) != (M, N) or tuple(out.shape) != (M, N):
         raise ValueError("R and out must be [M, N]")
+    _check_aliasing((X, planes, absmax, codebook), R, out)
     return M, N, K
 
 

@@ -257,6 +257,18 @@ def test_misaligned_and_bad_arguments_raise(sk):
         sk.addmm(Xd, Wd.t(), Rd)
     with pytest.raises(ValueError):
         sk.addmm(Xd.cpu(), Wd, Rd)
+    # the output may be R itself, but never overlap X or W or only part of R
+    buf = torch.zeros(2 * 72 + 2 * 64 + 16, dtype=torch.bfloat16, device="cuda")
+    Xa = buf[:2 * 72].view(2, 72)
+    Xa.copy_(Xd)
+    with pytest.raises(ValueError):
+        sk.addmm(Xa, Wd, Rd, out=buf[2 * 72 - 8:2 * 72 - 8 + 2 * 64].view(2, 64))
+    Rb = buf[2 * 72:2 * 72 + 2 * 64].view(2, 64)
+    Rb.copy_(Rd)
+    with pytest.raises(ValueError):
+        sk.addmm(Xd, Wd, Rb, out=buf[2 * 72 + 8:2 * 72 + 8 + 2 * 64].view(2, 64))
+    with pytest.raises(ValueError):
+        sk.addmm(Xd, Wd, Rd, out=Wd.view(-1)[:2 * 64].view(2, 64))
     Xk = torch.zeros((2, 12), dtype=torch.bfloat16, device="cuda")
     Wk = torch.zeros((64, 12), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError):
