@@ -4,9 +4,13 @@
 // Operation: vLLM benchmark page "benchmarks/kernels/benchmark_k3_cutedsl_residual.py"
 // (module docstring; torch.addmm leg): Y = bf16(X W^T + R), fp32 accumulation.
 // Design for gfx950:
-//   * a workgroup of 4 waves computes a BN x BM block of Y^T (BN rows of W, BM rows of X);
-//     the waves sit in a 2 x 2 layout, each a (BN/2) x (BM/2) block of
-//     v_mfma_f32_16x16x32_bf16 tiles;
+//   * a workgroup of 4 waves computes a BN x BM block of Y^T (BN rows of W, BM rows of X)
+//     with v_mfma_f32_16x16x32_bf16 tiles, split over the waves in one of two ways:
+//     KW = false: a 2 x 2 layout, each wave a (BN/2) x (BM/2) block over the whole stage
+//     (every fragment is read from LDS by the two waves that share it);
+//     KW = true: each wave takes one of the stage's four 32-wide K steps for the whole block
+//     (every fragment is read once; the waves' partial blocks are added in the epilogue,
+//     in wave order);
 //   * K advances in stages of 128. A stage is (BN + BM) rows of 256 bytes in LDS, held in a
 //     ring of NS stages. Each wave moves its share of a stage with direct-to-LDS loads
 //     (16 bytes per lane, 1 KB of LDS per instruction, four 256-byte rows), so operand
@@ -19,8 +23,9 @@
 //     its own loads of the stage with an explicit vmcnt count, then one barrier publishes
 //     the stage to the workgroup and frees the slot read in the previous iteration, which
 //     is refilled right after the barrier;
-//   * each stage sums into a fresh tile that is then added to the total, so the longest
-//     fp32 rounding chain is 4 + K/128 additions;
+//   * KW = false: each stage sums into a fresh tile that is then added to the total, so the
+//     longest fp32 rounding chain is 4 + K/128 additions; KW = true: K/128 accumulations per
+//     wave, then the three additions of the wave partials;
 //   * block ids are laid out so that the M-tiles of one W row tile are consecutive on one XCD
 //     (blocks are dealt to the 8 XCDs round-robin): they share the W tile through that
 //     XCD's L2, so W leaves HBM once;
@@ -63,14 +68,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// BN: rows of W per workgroup; BM: rows of X per workgroup; NS: LDS stages in the ring.
-template <int BN, int BM, int NS, bool ACC, bool GEN>
+// BN: rows of W per workgroup; BM: rows of X per workgroup; NS: LDS stages in the ring;
+// KW: the waves split each stage's K steps (true) or the block (false).
+template <int BN, int BM, int NS, bool KW, bool ACC, bool GEN>
 __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ W,
                                                        const uint16_t *R, void *out,
                                                        int M, int N, int K, int n_tiles, int m_tiles, Epilogue ep) {
     const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
-    constexpr int WN = BN / 2, WM = BM / 2;          // wave block
+    constexpr int WN = KW ? BN : BN / 2, WM = KW ? BM : BM / 2;  // wave block
     constexpr int TN = WN / 16, TM = WM / 16;        // MFMA tiles per wave
     static_assert(TN >= 1 && TM >= 1, "tile too small");
     constexpr int ROWS = BN + BM;                    // staged rows: W rows, then X rows
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
     static_assert(BLOCKS % 4 == 0, "stage blocks must split evenly over 4 waves");
     constexpr int PW = BLOCKS / 4;                   // load instructions per wave per stage
     static_assert(PW * (NS - 2) < 64 && NS >= 2, "vmcnt budget");
-    constexpr int CBYTES = BN * (BM + 4) * 4;        // fp32 block for the epilogue (padded)
+    constexpr int CBYTES = (KW ? 4 : 1) * BN * (BM + 4) * 4;  // fp32 block(s) for the epilogue (padded)
     constexpr int LDS_BYTES = NS * STAGE_BYTES > CBYTES ? NS * STAGE_BYTES : CBYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wn = (wave & 1) * WN, wm = (wave >> 1) * WM;
+    const int wn = KW ? 0 : (wave & 1) * WN, wm = KW ? 0 : (wave >> 1) * WM;
     const int S = K / kKC;                           // stages (K % 128 == 0)
 
     // This lane's source row and chunk for each of the wave's load blocks. Block q covers
@@ -156,6 +162,20 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
         if (s + NS - 1 < S) issue(s + NS - 1);
         const uint8_t *Ws = lds + (s % NS) * STAGE_BYTES;
         const uint8_t *Xs = Ws + BN * kRowBytes;
+        if constexpr (KW) {
+            // this wave's K step of the stage, every tile of the block, straight into acc
+            const int off = (((4 * wave + fq) ^ frow) << 4) + frow * kRowBytes;
+            u32x4_t af[TN], bfr[TM];
+#pragma unroll
+            for (int a = 0; a < TN; ++a) af[a] = *reinterpret_cast<const u32x4_t *>(Ws + 16 * a * kRowBytes + off);
+#pragma unroll
+            for (int c = 0; c < TM; ++c) bfr[c] = *reinterpret_cast<const u32x4_t *>(Xs + 16 * c * kRowBytes + off);
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int c = 0; c < TM; ++c) acc[a][c] = mfma16(af[a], bfr[c], acc[a][c]);
+            continue;
+        }
         f32x4_t st[TN][TM];
 #pragma unroll
         for (int a = 0; a < TN; ++a)
@@ -185,13 +205,15 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
     // epilogue: acc[a][c][r] = Y^T[n0 + wn + 16a + 4*(lane/16) + r][m0 + wm + 16c + lane%16]
     __syncthreads();                                 // every wave is done with the ring
     float *C = reinterpret_cast<float *>(lds);       // C[n][m], row pitch BM + 4 floats
+    constexpr int CB = BN * (BM + 4);                // floats per block copy
+    float *Cw = C + (KW ? wave * CB : 0);            // KW: one partial block per wave
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
         for (int c = 0; c < TM; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                C[(wn + 16 * a + 4 * (lane >> 4) + r) * (BM + 4) + wm + 16 * c + (lane & 15)] = acc[a][c][r];
+                Cw[(wn + 16 * a + 4 * (lane >> 4) + r) * (BM + 4) + wm + 16 * c + (lane & 15)] = acc[a][c][r];
     __syncthreads();
     // walk the block row by row of Y: neighbouring threads take neighbouring n
 #pragma unroll
@@ -200,12 +222,15 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
         const int ml = e / BN, nl = e % BN;
         const int m = m0 + ml, n = n0 + nl;
         if (m < M && n < N) {
-            store_output<ACC>(out, epi, m, n, C[nl * (BM + 4) + ml], bf16_bits_to_f32(rv[i]));
+            float t = C[nl * (BM + 4) + ml];
+            if constexpr (KW) t = ((t + C[CB + nl * (BM + 4) + ml]) + C[2 * CB + nl * (BM + 4) + ml]) +
+                                  C[3 * CB + nl * (BM + 4) + ml];
+            store_output<ACC>(out, epi, m, n, t, bf16_bits_to_f32(rv[i]));
         }
     }
 }
 
-template <int BN, int BM, int NS>
+template <int BN, int BM, int NS, bool KW>
 hipError_t launch_dma(const LaunchArgs &a) {
     const int n_tiles = (int)((a.N + BN - 1) / BN);
     const int m_tiles = (int)((a.M + BM - 1) / BM);
@@ -213,13 +238,13 @@ hipError_t launch_dma(const LaunchArgs &a) {
     dim3 grid((unsigned)(groups * 8 * m_tiles));
     dim3 block(256);
     if (a.acc_out)
-        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, true, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, KW, true, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
                            a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     else if (plain_epilogue(a))
-        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false, false>), grid, block, 0, a.stream, a.X, a.W, a.R,
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, KW, false, false>), grid, block, 0, a.stream, a.X, a.W, a.R,
                            a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     else
-        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, false, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
+        hipLaunchKernelGGL((mfma_dma_kernel<BN, BM, NS, KW, false, true>), grid, block, 0, a.stream, a.X, a.W, a.R,
                            a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep);
     return hipGetLastError();
 }
@@ -227,13 +252,15 @@ hipError_t launch_dma(const LaunchArgs &a) {
 int64_t dma_max_k() { return INT64_MAX; }
 
 // Public knobs: path SKINNY_PATH_GEMM_DMA, block_size = 256, outputs_per_block = BN,
-// k_unroll = NS (LDS stages in the ring), vector_width = 8, m_tile = BM, k_split = 1.
-#define DMA_ENTRY(BN, BM, NS)                                                                      \
+// k_unroll = NS (LDS stages in the ring), vector_width = 8, m_tile = BM, k_split = 1 for the
+// 2 x 2 wave layout or 4 for the four waves splitting each stage's K steps.
+#define DMA_ENTRY_K(BN, BM, NS, KW)                                                                \
     KernelEntry {                                                                                  \
-        skinny_config{SKINNY_PATH_GEMM_DMA, 256, BN, NS, 8, BM, 1}, &launch_dma<BN, BM, NS>,       \
-            (const void *)&mfma_dma_kernel<BN, BM, NS, false, false>,                              \
-            (const void *)&mfma_dma_kernel<BN, BM, NS, true, true>, &dma_max_k, kKC                \
+        skinny_config{SKINNY_PATH_GEMM_DMA, 256, BN, NS, 8, BM, (KW) ? 4 : 1},                     \
+            &launch_dma<BN, BM, NS, KW>, (const void *)&mfma_dma_kernel<BN, BM, NS, KW, false, false>, \
+            (const void *)&mfma_dma_kernel<BN, BM, NS, KW, true, true>, &dma_max_k, kKC            \
     }
+#define DMA_ENTRY(BN, BM, NS) DMA_ENTRY_K(BN, BM, NS, false)
 
 const KernelEntry kDmaEntries[] = {
     DMA_ENTRY(32, 32, 4),
@@ -245,6 +272,13 @@ const KernelEntry kDmaEntries[] = {
     DMA_ENTRY(128, 64, 2),
     DMA_ENTRY(128, 64, 3),
     DMA_ENTRY(64, 128, 3),
+    DMA_ENTRY_K(32, 32, 4, true),
+    DMA_ENTRY_K(32, 64, 4, true),
+    DMA_ENTRY_K(64, 32, 4, true),
+    DMA_ENTRY_K(64, 64, 3, true),
+    DMA_ENTRY_K(64, 64, 4, true),
+    DMA_ENTRY_K(128, 64, 3, true),
+    DMA_ENTRY_K(64, 128, 3, true),
 };
 
 }  // namespace

@@ -68,8 +68,10 @@ enum {
                                  k_unroll tiles per step, X loaded through the cache; any K.
                                  Built for the page-1 sweep grid at m_tile 16 */
     SKINNY_PATH_GEMM_DMA = 5  /* matrix-core K-loop GEMM whose operand tiles are loaded from
-                                 memory straight into a ring of LDS stages (k_unroll = stages);
-                                 K must be a multiple of 128 (else SKINNY_ENOTSUP) */
+                                 memory straight into a ring of LDS stages (k_unroll = stages;
+                                 k_split 4: the 4 waves split each stage's K steps, 1: they
+                                 split the output block); K must be a multiple of 128 (else
+                                 SKINNY_ENOTSUP) */
 };
 
 /*
