@@ -290,7 +290,8 @@ def oracle_parity_sample(wl, launch, count=512):
 
 
 def cpu_baseline(M: int, seconds: float):
-    """The CPU oracle, as it stands, on full calls of the same workload (copy 0)."""
+    """The CPU oracle, as it stands, on full calls of the same workload (copy 0), on the host's
+    usable threads; a shorter sample on one thread is reported beside it."""
     import oracle
     from decode_skinny_addmm_amd import synth
     X, ws, rs = synth.make_inputs(M, N_DIM, K_DIM)
@@ -299,19 +300,28 @@ def cpu_baseline(M: int, seconds: float):
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit():
         threads = min(threads, int(omp))
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.addmm_bf16(Xb, Wb, Rb, threads=threads, want_acc=False)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def timed(nthreads, budget):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.addmm_bf16(Xb, Wb, Rb, threads=nthreads, want_acc=False)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return calls, el
+
+    calls, el = timed(threads, seconds)
     per_call = el / calls
+    calls1, el1 = timed(1, max(1.0, seconds / 4))
+    per_call1 = el1 / calls1
     return {"value": algorithmic_bytes(M) / per_call / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle", "us_per_call": per_call * 1e6,
             "sample": "%d full calls (M=%d, N=%d, K=%d, copy 0) in %.1f s on %d threads" % (
-                calls, M, N_DIM, K_DIM, el, threads)}
+                calls, M, N_DIM, K_DIM, el, threads),
+            "one_thread": {"value": algorithmic_bytes(M) / per_call1 / 1e9, "unit": "GB/s",
+                           "us_per_call": per_call1 * 1e6,
+                           "sample": "%d full calls in %.1f s on 1 thread" % (calls1, el1)}}
 
 
 def probe_launches(sk):
