@@ -279,6 +279,9 @@ const KernelEntry kDmaEntries[] = {
     DMA_ENTRY_K(64, 64, 4, true),
     DMA_ENTRY_K(128, 64, 3, true),
     DMA_ENTRY_K(64, 128, 3, true),
+    // 32 W rows by as many X rows as M needs: 224 workgroups for N = 7168, W read once
+    DMA_ENTRY_K(32, 48, 4, true),
+    DMA_ENTRY_K(32, 80, 4, true),
 };
 
 }  // namespace

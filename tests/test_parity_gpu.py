@@ -99,7 +99,7 @@ def sample_positions(M, N, count, seed):
     return np.array(ms, np.int64), np.array(ns, np.int64)
 
 
-@pytest.mark.parametrize("M", [26, 32, 64, 128, 256])
+@pytest.mark.parametrize("M", [26, 32, 48, 64, 80, 128, 256])
 def test_full_size_sampled(sk, M):
     """Larger M at the selected configuration: sampled outputs against the oracle, every
     output against an fp32 GPU product within a bound that any correct fp32 sum meets."""
