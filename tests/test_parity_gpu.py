@@ -277,8 +277,8 @@ def test_misaligned_and_bad_arguments_raise(sk):
 
 # ------------------------------------------------------------------ determinism and graphs
 
-def test_deterministic_and_default_entry(sk):
-    M = 4
+@pytest.mark.parametrize("M", [4, 64, 256])
+def test_deterministic_and_default_entry(sk, M):
     X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL)
     Xd, Wd, Rd = _dev(X, ws[0], rs[0])
     a = sk.addmm(Xd, Wd, Rd)
@@ -289,8 +289,9 @@ def test_deterministic_and_default_entry(sk):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_graph_replay_matches_eager(sk):
-    M = 4
+@pytest.mark.parametrize("M", [4, 64, 256])
+def test_graph_replay_matches_eager(sk, M):
+    print("graph replay M=%d config %s" % (M, sk.select_config(M)), flush=True)
     X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL, copies=3)
     Xd = X.cuda()
     Wds = [w.cuda() for w in ws]
