@@ -14,7 +14,9 @@
 //   * K advances in stages of 128. A stage is (BN + BM) rows of 256 bytes in LDS, held in a
 //     ring of NS stages. Each wave moves its share of a stage with direct-to-LDS loads
 //     (16 bytes per lane, 1 KB of LDS per instruction, four 256-byte rows), so operand
-//     bytes never pass through registers and no LDS store instructions are issued;
+//     bytes never pass through registers and no LDS store instructions are issued; load i of
+//     every wave covers rows 16i .. 16i + 15, so the W rows (read once) take the non-temporal
+//     cache policy and the X rows (read by every W tile) the default one;
 //   * the 16-byte chunks of a row are stored XOR-swizzled by the row index (chunk c of row r
 //     sits at position c ^ (r & 15)): a lane's load still covers a 64-byte aligned piece of
 //     one row, and the MFMA fragment reads (16 rows, one logical chunk) hit 16 distinct
@@ -104,26 +106,32 @@ __global__ __launch_bounds__(256) void mfma_dma_kernel(const uint16_t *__restric
     const int wn = KW ? 0 : (wave & 1) * WN, wm = KW ? 0 : (wave >> 1) * WM;
     const int S = K / kKC;                           // stages (K % 128 == 0)
 
-    // This lane's source row and chunk for each of the wave's load blocks. Block q covers
-    // staged rows 4q..4q+3; lane l fills position l: row 4q + l/16, stored chunk l%16, which
-    // holds logical chunk (l%16) ^ (row & 15). Rows past M or N re-read the last valid row
-    // (their outputs are never written).
+    // This lane's source row and chunk for each of the wave's load blocks. Block q = 4i + wave
+    // covers staged rows 4q..4q+3; lane l fills position l: row 4q + l/16, stored chunk l%16,
+    // which holds logical chunk (l%16) ^ (row & 15). Rows past M or N re-read the last valid
+    // row (their outputs are never written).
     const uint16_t *src[PW];
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-        const int q = wave * PW + i;
+        const int q = 4 * i + wave;                  // load i of every wave covers rows 16i..16i+15
         const int sr = 4 * q + (lane >> 4);
         const int c = (lane & 15) ^ (sr & 15);
         const uint16_t *row = sr < BN ? W + (size_t)min(n0 + sr, N - 1) * K
                                       : X + (size_t)min(m0 + sr - BN, M - 1) * K;
         src[i] = row + 8 * c;
     }
+    static_assert(BN % 16 == 0, "W loads are whole 16-row groups");
     auto issue = [&](int s) {                        // stage s -> ring slot s % NS
-        lds_void *dst = (lds_void *)(lds + (s % NS) * STAGE_BYTES + wave * PW * 1024);
+        uint8_t *st = lds + (s % NS) * STAGE_BYTES + wave * 1024;
 #pragma unroll
-        for (int i = 0; i < PW; ++i)
+        for (int i = 0; i < BN / 16; ++i)            // W rows: read once, non-temporal
             __builtin_amdgcn_global_load_lds((const void *)(src[i] + (size_t)s * kKC),
-                                             (lds_void *)((__attribute__((address_space(3))) uint8_t *)dst + i * 1024),
+                                             (lds_void *)((__attribute__((address_space(3))) uint8_t *)st + i * 4096),
+                                             16, 0, 2);
+#pragma unroll
+        for (int i = BN / 16; i < PW; ++i)           // X rows: shared by every W tile, cached
+            __builtin_amdgcn_global_load_lds((const void *)(src[i] + (size_t)s * kKC),
+                                             (lds_void *)((__attribute__((address_space(3))) uint8_t *)st + i * 4096),
                                              16, 0, 0);
     };
 
