@@ -240,6 +240,9 @@ const KernelEntry kMfmaLdsEntries[] = {
     MFMA_LDS_ENTRY(7, 16, 2, 2, true, false),
     MFMA_LDS_ENTRY(7, 16, 2, 2, true, true),
     MFMA_LDS_ENTRY(7, 8, 4, 2, true, true),
+    // few rows per workgroup: enough workgroups for one rank's narrow share of N
+    MFMA_LDS_ENTRY(7, 4, 1, 1, true, true),
+    MFMA_LDS_ENTRY(7, 8, 1, 1, true, true),
 };
 
 }  // namespace
