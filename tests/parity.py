@@ -6,8 +6,12 @@ random data):
   * Y: at most 2 bf16 ULP from the oracle's correctly rounded value wherever
     |Y_exact| >= TAU = 2^-12; below TAU (cancellation, where an fp32 sum's absolute
     error is comparable to a bf16 ULP) |Y - Y_exact| <= 2 * ulp_bf16(TAU) = 2^-18.
-  * ACC (the fp32 value before rounding): |ACC - Y_exact| <= 1e-4 * max(|Y_exact|, 1e-2),
-    and Y must equal RNE_bf16(ACC) exactly (the epilogue is a single rounding).
+  * ACC (the fp32 value before rounding): |ACC - Y_exact| <= 1e-4 * max(|Y_exact|, 0.1),
+    and Y must equal RNE_bf16(ACC) exactly (the epilogue is a single rounding). The floor is
+    a tenth of the unit output scale: an fp32 sum's error follows the size of its partial
+    sums (unit scale here; each rounding of one is up to 6e-8), not the size of the result,
+    so below the floor the bar is 1e-5 absolute. That still sits 200x below one bf16
+    rounding of a partial sum (2^-9) and 1700x below one dropped product.
 Exact-input cases (X = 0, one-hot W rows, small integers) are compared bit-for-bit.
 """
 from __future__ import annotations
@@ -18,7 +22,7 @@ import torch
 TAU = 2.0 ** -12
 ABS_FLOOR = 2.0 ** -18
 ACC_REL = 1e-4
-ACC_FLOOR = 1e-2
+ACC_FLOOR = 0.1
 
 
 def bits_of(t: torch.Tensor) -> np.ndarray:
