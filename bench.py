@@ -12,7 +12,11 @@ functions graph_samples / summarize / rotating_buffer_count, re-done for HIP):
 
 Default run (no flags): M = 4, 6 copies, 500 calls per graph, prints ONE JSON line with
 the throughput (algorithmic HBM GB/s), the roofline fraction against 8 TB/s and the CPU
-oracle timed on this host as a baseline.
+oracle timed on this host as a baseline. The same line carries `curve`: the metric at
+M = 1, 2, 4, ..., 256 (each M on its own seeded inputs and rotation, the library's selected
+configuration; median/p10/p90 us, GB/s, HBM and MFMA fractions, a sampled oracle check, and
+the one-copy cache-warm time), and `m64_valu_vs_mfma`: the pages' SIMT GEMV at its best grid
+point against the matrix-core path at M = 64.
 
 Other modes write JSONL rows (one per configuration or M) to --out:
   --mode sweep    every built configuration at --m (default 16)
@@ -342,6 +346,24 @@ def probe_launches(sk):
     return null, read
 
 
+def probe_rows_and_spin(sk):
+    """The GEMV-shaped read (every load issued first) and the busy-kernel launch probe."""
+    import torch
+    L = sk.ops.lib()
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def read_rows(X, W, R, Y, rpb=32):
+        sk.ops.check(L.skinny_probe_read_rows(W.data_ptr(), W.shape[0], rpb, sink.data_ptr(), cur()),
+                     "skinny_probe_read_rows")
+
+    def spin(X, W, R, Y, ns=4000, blocks=224, threads=448):
+        sk.ops.check(L.skinny_probe_spin(ns, blocks, threads, cur()), "skinny_probe_spin")
+    return read_rows, spin
+
+
 def reference_rows(sk, wl, calls, warmup, steps):
     """Per-launch floor and the streaming-read rate over the same rotating W copies."""
     null, read = probe_launches(sk)
@@ -352,7 +374,18 @@ def reference_rows(sk, wl, calls, warmup, steps):
         per, total_ms = time_graph(lambda X, W, R, Y, u=u: read(X, W, R, Y, u), wl, calls, warmup, steps)
         us = total_ms * 1000.0 / (steps * calls)
         out["stream_read_u%d" % u] = {"us": us, "gbs": wl.N * wl.K * 2 / (us * 1e-6) / 1e9}
-    best = max(v["gbs"] for k, v in out.items() if k.startswith("stream_read"))
+    read_rows, spin = probe_rows_and_spin(sk)
+    if wl.K == K_DIM:
+        for rpb in (32, 28, 16, 8):
+            per, total_ms = time_graph(lambda X, W, R, Y, r=rpb: read_rows(X, W, R, Y, r), wl, calls, warmup, steps)
+            us = total_ms * 1000.0 / (steps * calls)
+            out["read_rows_rpb%d" % rpb] = {"us": us, "gbs": wl.N * wl.K * 2 / (us * 1e-6) / 1e9,
+                                            "workgroups": -(-wl.N // rpb)}
+    for ns in (4000, 8000):
+        per, total_ms = time_graph(lambda X, W, R, Y, n=ns: spin(X, W, R, Y, n), wl, calls, warmup, steps)
+        us = total_ms * 1000.0 / (steps * calls)
+        out["spin_%dns_224x448" % ns] = {"us": us, "overhead_us": us - ns / 1000.0}
+    best = max(v["gbs"] for k, v in out.items() if k.startswith("stream_read") or k.startswith("read_rows"))
     out["stream_read_best_gbs"] = best
     return out
 
@@ -441,6 +474,53 @@ def measure(sk, wl, config, calls, warmup, steps):
     return launch, us_per_call, mean_us, gbs
 
 
+CURVE_MS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+# The best point of the pages' SIMT grid at M = 64 (block 64, 8 outputs per block, k-unroll 1,
+# 16-byte vectors, 16-row X tile), timed beside the library's matrix-core choice.
+SIMT_BEST_M64 = {"path": 4, "block_size": 64, "outputs_per_block": 8, "k_unroll": 1, "vector_width": 8,
+                 "m_tile": 16, "k_split": 1}
+
+
+def curve_point(sk, wl, cfg, calls, warmup, steps, one_copy=True):
+    """One M of the metric's curve: rotated (the metric) and one-copy cache-warm timings."""
+    M = wl.M
+    launch, samples, mean_us, gbs = measure(sk, wl, cfg, calls, warmup, steps)
+    st = summarize(samples)
+    flops = 2.0 * M * wl.N * wl.K
+    row = {"M": M, "config": cfg, "us": round(mean_us, 4),
+           "median_us": round(st["median_us"], 4), "p10_us": round(st["p10_us"], 4),
+           "p90_us": round(st["p90_us"], 4), "cv_pct": round(st["cv_pct"], 3),
+           "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+           "frac_mfma": round(flops / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+           "max_ulp_sampled": oracle_parity_sample(wl, launch, 256)}
+    if one_copy:
+        _, _, one_us, _ = measure(sk, OneCopy(wl), cfg, calls, warmup, steps)
+        row["one_copy_cache_warm_us"] = round(one_us, 4)
+    return row
+
+
+def run_curve(args, sk):
+    """The metric over M = 1 ... 256 at the library's selected configuration, each M on its own
+    seeded inputs (6 rotating copies), plus the M = 64 comparison of the pages' SIMT GEMV with
+    the matrix-core path."""
+    import torch
+    curve, m64 = [], None
+    steps, warmup = max(5, args.steps // 2), max(2, args.warmup)
+    for M in CURVE_MS:
+        wl = Workload(M, args.copies)
+        row = curve_point(sk, wl, sk.select_config(M), args.calls, warmup, steps)
+        log("curve " + json.dumps(row))
+        curve.append(row)
+        if M == 64:
+            simt = curve_point(sk, wl, SIMT_BEST_M64, args.calls, warmup, steps, one_copy=False)
+            m64 = {"valu_simt_best": simt, "mfma_selected": row,
+                   "mfma_speedup": round(simt["us"] / row["us"], 3)}
+            log("m64 " + json.dumps(m64))
+        del wl
+        torch.cuda.empty_cache()
+    return curve, m64
+
+
 def run_default(args, sk):
     import torch
     M = args.m
@@ -494,6 +574,10 @@ def run_default(args, sk):
         row["secondary_correctness"] = secondary_correctness(wl, launch)
     except Exception as e:  # noqa: BLE001
         row["parity_error"] = "%s: %s" % (type(e).__name__, e)
+    if not args.no_curve:
+        del wl
+        torch.cuda.empty_cache()
+        row["curve"], row["m64_valu_vs_mfma"] = run_curve(args, sk)
     if not args.no_cpu_baseline:
         row["cpu_baseline"] = cpu_baseline(M, args.cpu_seconds)
     print(json.dumps(row), flush=True)
@@ -770,6 +854,7 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-reference", action="store_true", help="skip the null/stream-read reference rows")
+    p.add_argument("--no-curve", action="store_true", help="default mode: skip the M = 1 ... 256 curve")
     p.add_argument("--ms", type=str, default=None, help="comma-separated M list for sweep/mcurve")
     p.add_argument("--n", type=int, default=N_DIM, help="sweep/mcurve: N (rows of W); the default run uses 7168")
     p.add_argument("--k", type=int, default=K_DIM, help="sweep/mcurve: K; the default run uses 3584")

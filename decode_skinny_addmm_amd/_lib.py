@@ -25,7 +25,8 @@ EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with
             "skinny_kbit_gemv_bf16", "skinny_kbit_gemv_bf16_acc_f32", "skinny_kda_verify_bf16",
             "skinny_num_configs", "skinny_get_config",
             "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
-            "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy")
+            "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy",
+            "skinny_probe_read_rows", "skinny_probe_spin")
 
 
 class SkinnyConfig(ctypes.Structure):
@@ -97,7 +98,10 @@ def lib() -> ctypes.CDLL:
     L.skinny_probe_null.argtypes = [vp]
     L.skinny_probe_read.argtypes = [vp, i64, vp, ctypes.c_int32, ctypes.c_int32, vp]
     L.skinny_probe_copy.argtypes = [vp, vp, i64, vp]
-    for f in ("skinny_probe_null", "skinny_probe_read", "skinny_probe_copy"):
+    L.skinny_probe_read_rows.argtypes = [vp, i64, ctypes.c_int32, vp, vp]
+    L.skinny_probe_spin.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, vp]
+    for f in ("skinny_probe_null", "skinny_probe_read", "skinny_probe_copy", "skinny_probe_read_rows",
+              "skinny_probe_spin"):
         getattr(L, f).restype = ctypes.c_int
     for f in ("skinny_addmm_bf16", "skinny_addmm_bf16_with_config", "skinny_addmm_bf16_acc_f32",
               "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",

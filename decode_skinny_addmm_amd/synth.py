@@ -100,40 +100,52 @@ def make_kbit_inputs(M: int, N: int = N_DEFAULT, K: int = K_DEFAULT, kbits: int 
     return X, planes, scales, rs, codebook
 
 
+def _kda_table(B: int, T: int, H: int, HV: int, K: int, V: int, ring_len: int):
+    """(name, shape, standard deviation, dtype) of every random input of one KDA verify step,
+    grouped as conv inputs, gate inputs, recurrent state, ring contents. Normal draws, taken
+    in this order from one generator, in fp32 and then converted to the listed dtype."""
+    dim = 2 * H * K + HV * V          # conv channels: q, k (H heads each) and v (HV heads)
+    slots = B + 1                     # state/ring slots and conv lines: one spare
+    bf, f32 = torch.bfloat16, torch.float32
+    return [
+        # conv1d: mixed projections of the T draft tokens, its taps and bias, the cached inputs
+        ("mixed", (B * T, dim), 0.5, bf),
+        ("w", (dim, 4), 0.3, bf),
+        ("bias", (dim,), 0.1, bf),
+        ("conv_pool", (slots, 3, dim), 1.0, bf),
+        # gate: per-token a (per K channel) and b (per value head), per-head A_log and dt_bias
+        ("a", (B * T, HV * K), 0.5, bf),
+        ("b", (B * T, HV), 1.0, bf),
+        ("A_log", (HV,), 0.5, f32),
+        ("dt_bias", (HV * K,), 0.5, f32),
+        # recurrent state [V, K] per slot and value head
+        ("ssm", (slots, HV, V, K), 0.2, f32),
+        # ring entries (overwritten by a ring-layout call; random, so unwritten ones show)
+        ("rawv", (slots, HV, ring_len, V), 1.0, bf),
+        ("rawk", (slots, H, ring_len, K), 1.0, bf),
+        ("g", (slots, HV, ring_len, K), 1.0, f32),
+        ("beta", (slots, HV, ring_len), 1.0, f32),
+    ]
+
+
 def make_kda_inputs(B: int, T: int = 4, H: int = 8, HV: int | None = None, K: int = 128, V: int = 128,
                     ring_len: int = 16, seed: int = 0):
-    """Inputs of one KDA chain-verify step with the distributions of the sglang page
-    "benchmark/kernels/bench_kda_verify_sweep.py" (make_inputs): bf16 mixed ~ 0.5 N(0,1)
-    [B*T, 2HK + HV V], conv weight 0.3 N [dim, 4], conv bias 0.1 N [dim], conv_pool N
-    [B+1, 3, dim], a 0.5 N [B*T, HV K], b N [B*T, HV]; float32 A_log 0.5 N [HV],
-    dt_bias 0.5 N [HV K], ssm 0.2 N [B+1, HV, V, K]; outputs win_pool and inter_ssm zero;
-    ring buffers rawv [B+1, HV, R, V], rawk [B+1, H, R, K] (bf16), g [B+1, HV, R, K],
-    beta [B+1, HV, R] (float32) N(0,1); cache_indices = inter_indices = 0..B-1.
-    Drawn on the host from a seeded generator; returns a dict of CPU tensors."""
+    """Inputs of one KDA chain-verify step with the shapes and distributions of the sglang page
+    "benchmark/kernels/bench_kda_verify_sweep.py" (its input maker): every random tensor of
+    _kda_table drawn from one CPU generator seeded 20260722 + 1000 B + seed (the page draws on
+    the GPU); the window and snapshot outputs zero-filled; cache and snapshot indices 0 .. B-1.
+    Returns a dict of CPU tensors."""
     HV = H if HV is None else HV
-    g = torch.Generator().manual_seed(20260722 + 1000 * B + seed)
+    g = torch.Generator().manual_seed(SEED_BASE + 1000 * B + seed)
+    out = {}
+    for name, shape, std, dtype in _kda_table(B, T, H, HV, K, V, ring_len):
+        out[name] = (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(dtype)
     dim = 2 * H * K + HV * V
-    lines = slots = B + 1
-    rnd = lambda *s, dt=torch.bfloat16: torch.randn(*s, generator=g, dtype=torch.float32).to(dt)
-    return {
-        "mixed": (rnd(B * T, dim, dt=torch.float32) * 0.5).to(torch.bfloat16),
-        "w": (rnd(dim, 4, dt=torch.float32) * 0.3).to(torch.bfloat16),
-        "bias": (rnd(dim, dt=torch.float32) * 0.1).to(torch.bfloat16),
-        "a": (rnd(B * T, HV * K, dt=torch.float32) * 0.5).to(torch.bfloat16),
-        "b": rnd(B * T, HV),
-        "A_log": rnd(HV, dt=torch.float32) * 0.5,
-        "dt_bias": rnd(HV * K, dt=torch.float32) * 0.5,
-        "conv_pool": rnd(lines, 3, dim),
-        "ssm": rnd(slots, HV, V, K, dt=torch.float32) * 0.2,
-        "win_pool": torch.zeros(lines, T, 3, dim, dtype=torch.bfloat16),
-        "inter_ssm": torch.zeros(lines, T, HV, V, K, dtype=torch.float32),
-        "rawv": rnd(slots, HV, ring_len, V),
-        "rawk": rnd(slots, H, ring_len, K),
-        "g": rnd(slots, HV, ring_len, K, dt=torch.float32),
-        "beta": rnd(slots, HV, ring_len, dt=torch.float32),
-        "cache_indices": torch.arange(B, dtype=torch.int32),
-        "inter_indices": torch.arange(B, dtype=torch.int32),
-    }
+    out["win_pool"] = torch.zeros(B + 1, T, 3, dim, dtype=torch.bfloat16)
+    out["inter_ssm"] = torch.zeros(B + 1, T, HV, V, K, dtype=torch.float32)
+    out["cache_indices"] = torch.arange(B, dtype=torch.int32)
+    out["inter_indices"] = torch.arange(B, dtype=torch.int32)
+    return out
 
 
 def kda_to_numpy(inp: dict) -> dict:

@@ -31,6 +31,23 @@ SKINNY_API skinny_status skinny_probe_null(void *stream);
 SKINNY_API skinny_status skinny_probe_read(const void *buf, int64_t bytes, float *sink,
                                            int32_t blocks, int32_t unroll, void *stream);
 
+/*
+ * Read `rows` rows of 7168 bytes at `buf` (16-byte aligned) the way the small-M kernels
+ * stream W at K = 3584: workgroups of 448 threads (7 waves) own `rows_per_block` (4, 8, 16,
+ * 28 or 32) contiguous rows, thread t loads 16-byte vector t of each row non-temporally, and
+ * every load of a workgroup is issued before any is used. The single-launch ceiling of that
+ * access pattern. `sink` as for skinny_probe_read.
+ */
+SKINNY_API skinny_status skinny_probe_read_rows(const void *buf, int64_t rows, int32_t rows_per_block,
+                                                float *sink, void *stream);
+
+/*
+ * Launch `blocks` workgroups of `threads` threads that each stay busy for `nanoseconds`
+ * (the 100 MHz real-time counter, so 10 ns steps) and touch no memory: call time minus
+ * that duration is what one launch costs around a kernel that is busy, not empty.
+ */
+SKINNY_API skinny_status skinny_probe_spin(int64_t nanoseconds, int32_t blocks, int32_t threads, void *stream);
+
 /* dst[0:bytes) = src[0:bytes) with 16-byte loads and stores (bytes % 16 == 0, both 16-B aligned). */
 SKINNY_API skinny_status skinny_probe_copy(void *dst, const void *src, int64_t bytes, void *stream);
 

@@ -62,6 +62,17 @@ def test_select_config_covers_all_m(L):
     assert L.skinny_select_config(-1, 1, 8, ctypes.byref(_lib.SkinnyConfig())) == 1
 
 
+@pytest.mark.parametrize("N", [7168, 896])
+def test_table_rows_resolve_without_fallback(L, N):
+    """At the tuned K every table row (full width and narrow) names a built instance: the
+    general fallbacks (direct MFMA, register GEMM) are only for K the table's kernels cannot
+    take, so selecting one here would mean a mistyped row."""
+    for M in list(range(1, 300)) + [1000]:
+        c = _lib.SkinnyConfig()
+        assert L.skinny_select_config(M, N, 3584, ctypes.byref(c)) == 0
+        assert c.as_dict()["path"] not in (1, 3), (M, N, c.as_dict())
+
+
 def test_get_config_range(L):
     c = _lib.SkinnyConfig()
     assert L.skinny_get_config(-1, ctypes.byref(c)) == 1

@@ -38,6 +38,14 @@ def sk():
     return d
 
 
+def near_midpoint(x, n_inp, B, T, dim):
+    """Conv values an fp32 evaluation may round differently from the fp64 one: within
+    2^-21 (sum of |terms| + |value|) of a bf16 rounding midpoint, eight times the unit
+    roundoff of an fp32 sum and silu (conv_term_magnitude gives the terms)."""
+    x = np.asarray(x, dtype=np.float64)
+    return midpoint_distance(x) < 2.0 ** -21 * (conv_term_magnitude(n_inp, B, T, dim) + np.abs(x))
+
+
 def midpoint_distance(x):
     """Distance of each float64 value to the nearest bf16 rounding midpoint."""
     x = np.abs(np.asarray(x, dtype=np.float64))
@@ -47,12 +55,17 @@ def midpoint_distance(x):
     return np.abs(frac - 0.5) * np.ldexp(1.0 / 256.0, e)
 
 
-def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True):
+def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True):
+    """One verify call against the oracle. clean: inputs moved away from conv rounding
+    midpoints first (clean_inputs), so every allowance below is empty and the bars are the
+    tight ones; otherwise the allowances cover values that fp32 and fp64 may round apart."""
     t_inp = synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V, seed=seed)
     if permute:
         lines = B + 1
         t_inp["cache_indices"] = torch.tensor([lines - 1 - i for i in range(B)], dtype=torch.int32)
         t_inp["inter_indices"] = torch.tensor([(i + 1) % lines for i in range(B)], dtype=torch.int32)
+    if clean:
+        t_inp = clean_inputs(t_inp, T, H, HV, K, V)
     n_inp = synth.kda_to_numpy(t_inp)
     scale = K ** -0.5
     print("kda", dict(B=B, T=T, H=H, HV=HV, K=K, V=V, ring=ring, seed=seed), flush=True)
@@ -62,17 +75,42 @@ def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True):
     ref = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=not ring, ring_len=16 if ring else 0)
     what = "kda B=%d T=%d H=%d HV=%d V=%d ring=%s" % (B, T, H, HV, V, ring)
     assert np.array_equal(synth.bits(d["win_pool"].cpu()), ref["win_pool"]), what + ": windows"
-    P.check_y(P.bits_of(o), ref["o"], ref["o_exact"], what + ": o")
     dim = 2 * H * K + HV * V
     conv_bits = oracle.round_bf16(ref["conv_exact"])
-    near = midpoint_distance(ref["conv_exact"]) < 1e-6
+    near = near_midpoint(ref["conv_exact"], n_inp, B, T, dim)
+    assert not (clean and near.any())
+    # o: the dense rule, except on (token, value head) whose q input at that token, or k or v
+    # input at that token or before, is near a midpoint: a one-step flip of q_c moves q^ by at
+    # most 2^-6 max|q^| in 2-norm, and a flip of k or v moves the state (see the snapshot
+    # allowances), so such o may move by up to 2^-5 scale sqrt(K) max|S| there
+    rows = near.reshape(B, T, dim)
+    qn = rows[:, :, :H * K].reshape(B, T, H, K).any(-1)
+    kn = np.cumsum(rows[:, :, H * K:2 * H * K].reshape(B, T, H, K).any(-1), axis=1) > 0
+    vn = np.cumsum(rows[:, :, 2 * H * K:].reshape(B, T, HV, V).any(-1), axis=1) > 0
+    group = HV // H
+    aff = np.repeat(qn | kn, group, axis=2) | vn                    # [B, T, HV]
+    aff = np.broadcast_to(aff.reshape(B * T, HV, 1), (B * T, HV, V))
+    og, oe = P.bits_of(o), ref["o_exact"]
+    P.check_y(og[~aff], ref["o"][~aff], oe[~aff], what + ": o")
+    if aff.any():
+        s_max = float(np.abs(ref["inter_ssm"] if not ring else n_inp["ssm"]).max()) * 4.0
+        lim_o = 2.0 ** -5 * scale * np.sqrt(K) * s_max
+        assert np.abs(oracle.bf16_bits_to_f64(og[aff]) - oe[aff]).max() <= lim_o, what + ": o near a flip"
     if ring:
+        # ring entry (slot cache_idx[b], head, position t, channel) holds conv output
+        # (row b*T + t, channel); only entries whose exact conv value is near a midpoint may differ
+        cidx = np.array([int(i) for i in n_inp["cache_indices"]])
+        near_rows = near.reshape(B, T, dim)
+        near_ring = {"rawv": np.zeros(ref["rawv"].shape, dtype=bool), "rawk": np.zeros(ref["rawk"].shape, dtype=bool)}
+        for bi in range(B):
+            near_ring["rawv"][cidx[bi], :, :T, :] = near_rows[bi, :, 2 * H * K:].reshape(T, HV, V).transpose(1, 0, 2)
+            near_ring["rawk"][cidx[bi], :, :T, :] = near_rows[bi, :, H * K:2 * H * K].reshape(T, H, K).transpose(1, 0, 2)
         for name in ("rawv", "rawk"):
             g = synth.bits(d[name].cpu()).astype(np.int64)
             r = ref[name].astype(np.int64)
             diff = np.abs(P.ordered(g) - P.ordered(r))
             assert diff.max() <= 1, what + ": " + name
-            assert (diff > 0).sum() <= int(near.sum()), what + ": %s differs away from a midpoint" % name
+            assert not (diff[~near_ring[name]] > 0).any(), what + ": %s differs away from a midpoint" % name
         assert np.allclose(d["g"].cpu().numpy(), ref["g"], rtol=1e-5, atol=1e-7), what + ": g"
         assert np.allclose(d["beta"].cpu().numpy(), ref["beta"], rtol=1e-5, atol=1e-7), what + ": beta"
     else:
@@ -122,6 +160,14 @@ def test_kda_page_shape(sk, B, ring):
     per workgroup at B = 1 and 4, 32 at B = 16 and 64 at B = 32 (128 at B = 64, in the ring test
     below)."""
     run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_kda_unfiltered_inputs(sk, ring):
+    """The page's layer on inputs as drawn (some conv outputs within an fp32 error of a bf16
+    midpoint): ring, snapshots and o within the bars widened only where such a value feeds
+    them."""
+    run_case(sk, 16, 4, 8, 8, 128, 128, ring, clean=False)
 
 
 def test_kda_gqa_page(sk):
@@ -195,3 +241,73 @@ def test_kda_poisoned_outputs_fully_written(sk, ring):
     else:
         assert not torch.isnan(d["inter_ssm"][lines]).any()
         assert torch.isnan(d["inter_ssm"][2]).all()
+
+
+def conv_term_magnitude(n_inp, B, T, dim):
+    """|bias| + sum over the four taps of |weight * input| for every conv output [B*T, dim]:
+    the scale of the fp32 rounding error of that output's sum."""
+    f = lambda b: oracle.bf16_bits_to_f64(b)
+    w, bias, pool, mixed = f(n_inp["w"]), f(n_inp["bias"]), f(n_inp["conv_pool"]), f(n_inp["mixed"])
+    cidx = [int(i) for i in n_inp["cache_indices"]]
+    mag = np.zeros((B * T, dim))
+    for bi in range(B):
+        seq = np.concatenate([pool[cidx[bi]], mixed[bi * T:(bi + 1) * T]], axis=0)   # [3 + T, dim]
+        for t in range(T):
+            mag[bi * T + t] = np.abs(bias) + sum(np.abs(w[:, j] * seq[t + j]) for j in range(4))
+    return mag
+
+
+def clean_inputs(t_inp, T, H, HV, K, V):
+    """The same inputs with every conv output moved away from bf16 rounding midpoints (judged
+    by the oracle's fp64 conv values with near_midpoint's margin): any token input feeding a
+    near-midpoint value is moved by 1/16 (doubling every fourth round, so that outputs too
+    small for any fp32 sum to round reliably leave that range) until none is left. The bf16 conv tensor
+    is then the same for any correct fp32 evaluation, and the parity bars need no midpoint
+    allowance."""
+    t_inp = {k: v.clone() for k, v in t_inp.items()}
+    B = int(t_inp["cache_indices"].shape[0])
+    dim = 2 * H * K + HV * V
+    for it in range(40):
+        n_inp = synth.kda_to_numpy(t_inp)
+        ref = oracle.kda_verify(n_inp, T, H, HV, K, V, K ** -0.5, snapshots=False)
+        near = near_midpoint(ref["conv_exact"], n_inp, B, T, dim)
+        if not near.any():
+            return t_inp
+        rows, cols = (torch.from_numpy(i) for i in np.nonzero(near))
+        m = t_inp["mixed"].float()
+        m[rows, cols] += 0.0625 * 2.0 ** (it // 4)
+        t_inp["mixed"] = m.to(torch.bfloat16)
+    raise AssertionError("could not move every conv output away from a midpoint")
+
+
+@pytest.mark.parametrize("B,H,HV,V", [(4, 8, 8, 128), (16, 8, 8, 128), (3, 2, 4, 32)])
+def test_kda_exact_conv_tight_bars(sk, B, H, HV, V):
+    """Inputs with every conv output away from a rounding midpoint, both layouts of the same
+    inputs: ring v and k equal to the oracle's bit for bit, g and beta within 1e-5, every
+    snapshot within 1e-5 |S| + 5e-4 rms(S) with no midpoint allowance, o within the dense rule."""
+    T, K = 4, 128
+    t_inp = clean_inputs(synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V, seed=11), T, H, HV, K, V)
+    n_inp = synth.kda_to_numpy(t_inp)
+    scale = K ** -0.5
+    what = "kda clean B=%d H=%d HV=%d V=%d" % (B, H, HV, V)
+    print(what, flush=True)
+    ref_s = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=True)
+    ref_r = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=False, ring_len=16)
+    ds = {k: v.cuda() for k, v in t_inp.items()}
+    o_s = sk.kda_verify(ds, T, H, HV, K, V, scale, snapshots=True, ring=False)
+    dr = {k: v.cuda() for k, v in t_inp.items()}
+    o_r = sk.kda_verify(dr, T, H, HV, K, V, scale, snapshots=False, ring=True)
+    torch.cuda.synchronize()
+    for name in ("rawv", "rawk"):
+        assert np.array_equal(synth.bits(dr[name].cpu()), ref_r[name]), what + ": " + name
+    assert np.allclose(dr["g"].cpu().numpy(), ref_r["g"], rtol=1e-5, atol=1e-7), what + ": g"
+    assert np.allclose(dr["beta"].cpu().numpy(), ref_r["beta"], rtol=1e-5, atol=1e-7), what + ": beta"
+    S = ds["inter_ssm"].cpu().numpy().astype(np.float64)
+    Se = ref_s["inter_ssm"]
+    rms = float(np.sqrt(np.mean(Se ** 2)))
+    err = np.abs(S - Se)
+    bad = err > 1e-5 * np.abs(Se) + 5e-4 * rms
+    assert not bad.any(), what + ": %d snapshot values off, max err %g (rms %g)" % (int(bad.sum()), err.max(), rms)
+    for o, ref in ((o_s, ref_s), (o_r, ref_r)):
+        P.check_y(P.bits_of(o), ref["o"], ref["o_exact"], what + ": o")
+    assert np.array_equal(synth.bits(ds["win_pool"].cpu()), ref_s["win_pool"])

@@ -99,22 +99,18 @@ def sample_positions(M, N, count, seed):
     return np.array(ms, np.int64), np.array(ns, np.int64)
 
 
-@pytest.mark.parametrize("M", [26, 32, 48, 64, 80, 128, 256])
-def test_full_size_sampled(sk, M):
-    """Larger M at the selected configuration: sampled outputs against the oracle, every
-    output against an fp32 GPU product within a bound that any correct fp32 sum meets."""
+@pytest.mark.parametrize("M", [17, 26, 32, 48, 64, 80, 128, 256])
+def test_full_size_full_oracle_large_m(sk, M):
+    """Every table row above M = 16 (and the M just past each boundary) at the full N x K
+    problem: every output against the oracle, at the selected configuration."""
     X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL)
-    print("full size sampled M=%d config %s" % (M, sk.select_config(M)), flush=True)
+    print("full size M=%d config %s" % (M, sk.select_config(M)), flush=True)
     Yg, Ag = run_both(sk, X, ws[0], rs[0])
-    ms, ns = sample_positions(M, N_FULL, 3000, M)
-    yo, ao = oracle.addmm_bf16_points(synth.bits(X), synth.bits(ws[0]), synth.bits(rs[0]), ms, ns)
-    P.check_y(Yg[ms, ns], yo, ao, "sampled M=%d" % M)
-    P.check_acc(Ag[ms, ns], ao, "sampled M=%d" % M)
+    Yo, Ao = full_oracle(X, ws[0], rs[0])
+    st = P.check_y(Yg, Yo, Ao, "M=%d" % M)
+    P.check_acc(Ag, Ao, "M=%d" % M)
     assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
-    # every output: within 1e-3 absolute of an fp32 product computed by torch on the GPU
-    Xd, Wd, Rd = _dev(X, ws[0], rs[0])
-    ref = (Xd.float() @ Wd.float().t() + Rd.float()).cpu().numpy().astype(np.float64)
-    assert np.abs(Ag - ref).max() < 1e-3
+    print(st)
 
 
 @pytest.mark.parametrize("M", [4, 16])

@@ -70,6 +70,42 @@ def test_shard_block_single_rounding(sk, M, N, K, ldr, c0r, ldy, c0y):
     assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
 
 
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 16, 24, 32])
+def test_shard_production_shape_selected(sk, M):
+    """One rank of an 8-way split of the 7168 output columns (N = 896, rank 3, R and Y as column
+    blocks of [M, 7168] matrices), K = 3584, at the configuration the library selects for that
+    shape (the narrow-output table), every output against the oracle. Flags off: the dense
+    rule. Flags on (two roundings, no -0): the fp32 sum meets the accumulator bar, Y is exactly
+    the two-rounding epilogue of that sum, and Y equals the oracle's twice-rounded output bit for
+    bit wherever the sum rounds to the same bf16 value as the exact sum."""
+    N, K, ld, c0 = 896, 3584, 7168, 896 * 3
+    print("shard production M=%d config %s" % (M, sk.select_config(M, N, K)), flush=True)
+    # flags off
+    X, W, R, Yg, Ag = shard_case(sk, M, N, K, ld, c0, ld, c0, 0, None, 1000 + M)
+    Yo, Ao = oracle.addmm_bf16(synth.bits(X), synth.bits(W), synth.bits(R))
+    P.check_y(Yg, Yo, Ao, "shard M=%d" % M)
+    P.check_acc(Ag, Ao, "shard M=%d" % M)
+    assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
+    # flags on, same inputs, same (selected) kernel
+    flags = ROUND | NONEG
+    _, _, _, Yf, Af = shard_case(sk, M, N, K, ld, c0, ld, c0, flags, None, 1000 + M)
+    _, Rz = wide(torch.zeros((M, N), dtype=torch.bfloat16), ld, c0, 0)
+    Sz = sk.addmm_shard_acc_f32(X.cuda(), W.cuda(), Rz).cpu().numpy().astype(np.float64)  # the fp32 sum
+    _, So = oracle.addmm_bf16(synth.bits(X), synth.bits(W), np.zeros((M, N), dtype=np.uint16))
+    P.check_acc(Sz, So, "shard sum M=%d" % M)
+    r = oracle.bf16_bits_to_f64(synth.bits(R))
+    gr = (oracle.bf16_bits_to_f64(oracle.round_bf16(Sz)).astype(np.float32) + r.astype(np.float32)).astype(np.float64)
+    assert np.array_equal(Af.astype(np.float64), gr), "ACC is not fp32(bf16(sum) + r)"
+    want = oracle.round_bf16(gr)
+    want = np.where(want == 0x8000, 0, want).astype(np.uint16)
+    assert np.array_equal(Yf, want), "Y is not the two-rounding epilogue of the fp32 sum"
+    assert not np.any(Yf == 0x8000)
+    Yof, _ = oracle.addmm_bf16(synth.bits(X), synth.bits(W), synth.bits(R), flags=flags)
+    same_sum = oracle.round_bf16(Sz) == oracle.round_bf16(So)
+    assert np.array_equal(Yf[same_sum], Yof[same_sum]), "differs from the oracle where the rounded sums agree"
+    assert same_sum.mean() > 0.99
+
+
 def test_shard_every_config(sk):
     """Every built configuration writes the strided block correctly (flags off and on)."""
     for (M, N, K) in [(5, 70, 512), (33, 130, 512)]:
