@@ -114,12 +114,14 @@ def parse_config(s: str | None):
     if not s:
         return None
     v = [int(t) for t in s.split(",")]
-    if len(v) not in (5, 6, 7):
-        raise argparse.ArgumentTypeError("config must be PATH,BLOCK,OUTPUTS,K_UNROLL,VECTOR_WIDTH[,M_TILE[,K_SPLIT]]")
-    keys = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
+    if len(v) not in (5, 6, 7, 8):
+        raise argparse.ArgumentTypeError("config must be PATH,BLOCK,OUTPUTS,K_UNROLL,VECTOR_WIDTH"
+                                         "[,M_TILE[,K_SPLIT[,K_STAGE]]]")
+    keys = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split", "k_stage")
     d = dict(zip(keys, v))
     d.setdefault("m_tile", 0)
     d.setdefault("k_split", 1)
+    d.setdefault("k_stage", 0)
     return d
 
 

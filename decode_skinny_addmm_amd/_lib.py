@@ -16,9 +16,11 @@ PATH_MFMA_LDS = 2
 PATH_GEMM = 3
 PATH_SIMT = 4
 PATH_GEMM_DMA = 5
+PATH_GEMM_RING = 6
 FLAG_ROUND_PRODUCT = 1  # shard epilogue: round the product sum to bf16, add R, round again
 FLAG_NO_NEG_ZERO = 2    # shard epilogue: write +0 for a -0 result
-CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split")
+CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split",
+                 "k_stage")
 
 EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with_config",
             "skinny_addmm_bf16_acc_f32", "skinny_addmm_bf16_shard", "skinny_addmm_bf16_shard_acc_f32",

@@ -30,6 +30,8 @@ struct Registry {
         for (int i = 0; i < n; ++i) all.push_back(&s[i]);
         const KernelEntry *d = dma_entries(&n);
         for (int i = 0; i < n; ++i) all.push_back(&d[i]);
+        const KernelEntry *g2 = ring_entries(&n);
+        for (int i = 0; i < n; ++i) all.push_back(&g2[i]);
     }
 };
 
@@ -41,7 +43,7 @@ const Registry &registry() {
 bool same_shape(const skinny_config &a, const skinny_config &b) {
     return a.path == b.path && a.block_size == b.block_size &&
            a.outputs_per_block == b.outputs_per_block && a.k_unroll == b.k_unroll &&
-           a.vector_width == b.vector_width && a.k_split == b.k_split;
+           a.vector_width == b.vector_width && a.k_split == b.k_split && a.k_stage == b.k_stage;
 }
 
 // Exact match; with m_tile == 0 the smallest built m_tile >= M (else the largest) is used.
@@ -109,7 +111,8 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
     const skinny_config c = cfg ? *cfg : select(M, N, K);
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
-        c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0)
+        c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0 ||
+        (c.path == SKINNY_PATH_GEMM_RING ? (c.k_stage != 64 && c.k_stage != 128) : c.k_stage != 0))
         return SKINNY_EINVAL;
     const KernelEntry *e = find_entry(c, M);
     if (!e) return SKINNY_ENOTSUP;

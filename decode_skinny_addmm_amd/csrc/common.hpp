@@ -75,6 +75,7 @@ const KernelEntry *mfma_lds_entries(int *count);
 const KernelEntry *gemm_entries(int *count);
 const KernelEntry *simt_entries(int *count);
 const KernelEntry *dma_entries(int *count);
+const KernelEntry *ring_entries(int *count);
 
 // ----------------------------------------------------------------------------- device helpers
 

@@ -67,11 +67,15 @@ enum {
                                  block_size * vector_width K-tile of outputs_per_block W rows,
                                  k_unroll tiles per step, X loaded through the cache; any K.
                                  Built for the page-1 sweep grid at m_tile 16 */
-    SKINNY_PATH_GEMM_DMA = 5  /* matrix-core K-loop GEMM whose operand tiles are loaded from
+    SKINNY_PATH_GEMM_DMA = 5, /* matrix-core K-loop GEMM whose operand tiles are loaded from
                                  memory straight into a ring of LDS stages (k_unroll = stages;
                                  k_split 4: the 4 waves split each stage's K steps, 1: they
                                  split the output block); K must be a multiple of 128 (else
                                  SKINNY_ENOTSUP) */
+    SKINNY_PATH_GEMM_RING = 6 /* the same operand pipeline with k_stage-wide stages (64 or 128)
+                                 and 4 or 8 waves (block_size 256 or 512); k_split = waves
+                                 taking alternate K steps of a stage, the others split the
+                                 block; K must be a multiple of k_stage (else SKINNY_ENOTSUP) */
 };
 
 /*
@@ -95,6 +99,8 @@ typedef struct skinny_config {
                                   library pick the smallest built tile >= M */
     int32_t k_split;           /* waves of a workgroup that share the same output columns
                                   and split K between them (their partial sums meet in LDS) */
+    int32_t k_stage;           /* K per LDS stage of SKINNY_PATH_GEMM_RING (64 or 128); 0 for
+                                  every other path */
 } skinny_config;
 
 /* Register and scratch use of one built configuration (hipFuncGetAttributes). */
