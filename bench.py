@@ -80,29 +80,25 @@ def kda_algorithmic_bytes(B: int, T: int, H: int, HV: int, K: int, V: int, ring:
     return state + states_out + ring_out + conv + gates + out
 
 
-def lookup_traffic(cfg: dict, M: int):
+def lookup_traffic(sk, cfg: dict, M: int, N: int = None, K: int = None):
     """HBM bytes per launch measured by rocprofv3 FETCH_SIZE/WRITE_SIZE runs for this exact
-    kernel configuration and M (profiles/traffic.json, scaled by a copy-kernel calibration);
-    None when absent or when the kernel source has changed since the counters were taken."""
-    import hashlib
+    kernel instance and shape (profiles/traffic.json, scaled by a copy-kernel calibration).
+    Entries are keyed by the kernel's name and the hash of its machine code in the build that
+    was measured, so the figure reads None as soon as that kernel's code changes."""
+    N = N_DIM if N is None else N
+    K = K_DIM if K is None else K
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         entries = json.load(open(path))["entries"]
-    except (OSError, ValueError, KeyError):
+        kern = sk.config_kernel(cfg)
+    except (OSError, ValueError, KeyError, RuntimeError):
         return None
     for e in entries:
-        if e.get("config") != cfg or e.get("M") != M or e.get("N") != N_DIM or e.get("K") != K_DIM:
-            continue
-        h = hashlib.sha256()
-        try:
-            for f in e["source_files"]:
-                h.update(open(os.path.join(ROOT, "decode_skinny_addmm_amd", "csrc", f), "rb").read())
-        except OSError:
-            return None
-        if h.hexdigest() != e.get("source_sha256"):
-            return None
-        return {"bytes": e["traffic_bytes"], "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
-                "source": "profiles/" + e["summary"]}
+        if (kern["name"] in (e.get("kernel"), e.get("kernel_mangled")) and kern["code_sha256"]
+                and e.get("code_sha256") == kern["code_sha256"]
+                and e.get("M") == M and e.get("N") == N and e.get("K") == K):
+            return {"bytes": e["traffic_bytes"], "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+                    "source": "profiles/" + e["summary"]}
     return None
 
 
@@ -549,13 +545,13 @@ def run_default(args, sk):
                                "W,R rotated over %d seeded copies; HIP graph of %d calls per step"
                                % (M, N_DIM, K_DIM, args.copies, args.calls),
                    "M": M, "N": N_DIM, "K": K_DIM, "copies": args.copies, "calls_per_step": args.calls,
-                   "kernel_config": cfg, "resources": res},
+                   "kernel_config": cfg, "resources": res, "kernel": sk.config_kernel(cfg)},
         "us_per_call": round(mean_us, 4),
         "us_per_call_stats": {k: round(v, 4) for k, v in st.items()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": (lambda t: t["bytes"] if t else None)(lookup_traffic(cfg, M)),
-                     "traffic_detail": lookup_traffic(cfg, M),
+                     "traffic": (lambda t: t["bytes"] if t else None)(lookup_traffic(sk, cfg, M)),
+                     "traffic_detail": lookup_traffic(sk, cfg, M),
                      "bytes_per_launch": algorithmic_bytes(M),
                      "mfma_frac": round(flops / (mean_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "device": torch.cuda.get_device_name(0),

@@ -8,7 +8,8 @@ call into it does, and raises if the library has not been built.
 from . import synth  # noqa: F401  (input generators; no arithmetic of the operation)
 
 __all__ = ["synth", "addmm", "addmm_default", "addmm_acc_f32", "addmm_shard", "addmm_shard_acc_f32",
-           "kbit_gemv", "kbit_gemv_acc_f32", "kda_verify", "select_config", "configs", "config_resources", "version"]
+           "kbit_gemv", "kbit_gemv_acc_f32", "kda_verify", "select_config", "configs", "config_resources", "version",
+           "config_kernel"]
 
 
 def __getattr__(name):
@@ -16,7 +17,8 @@ def __getattr__(name):
         import importlib
         return importlib.import_module(".ops", __name__)
     if name in ("addmm", "addmm_default", "addmm_acc_f32", "addmm_shard", "addmm_shard_acc_f32",
-                "kbit_gemv", "kbit_gemv_acc_f32", "kda_verify", "select_config", "configs", "config_resources", "version"):
+                "kbit_gemv", "kbit_gemv_acc_f32", "kda_verify", "select_config", "configs", "config_resources", "version",
+                "config_kernel"):
         from . import ops
         return getattr(ops, name)
     raise AttributeError(name)

@@ -28,7 +28,7 @@ EXPORTED = ("skinny_addmm_bf16", "skinny_select_config", "skinny_addmm_bf16_with
             "skinny_num_configs", "skinny_get_config",
             "skinny_config_resources", "skinny_status_string", "skinny_last_hip_error",
             "skinny_version", "skinny_probe_null", "skinny_probe_read", "skinny_probe_copy",
-            "skinny_probe_read_rows", "skinny_probe_spin")
+            "skinny_probe_read_rows", "skinny_probe_spin", "skinny_config_kernel_name")
 
 
 class SkinnyConfig(ctypes.Structure):
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.skinny_select_config.argtypes = [i64, i64, i64, cfgp]
     L.skinny_get_config.argtypes = [ctypes.c_int32, cfgp]
     L.skinny_config_resources.argtypes = [cfgp, ctypes.POINTER(SkinnyResources)]
+    L.skinny_config_kernel_name.argtypes = [cfgp, ctypes.c_char_p, ctypes.c_int32]
+    L.skinny_config_kernel_name.restype = ctypes.c_int
     L.skinny_status_string.argtypes = [ctypes.c_int]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_version.restype = ctypes.c_char_p

@@ -4,7 +4,8 @@
 
 Every .hip file in csrc/ is compiled to an object in parallel, then linked into
 decode_skinny_addmm_amd/libskinny.so. Packed-fp32 instructions are disabled for all
-device code (-packed-fp32-ops).
+device code (-packed-fp32-ops). kernel_code.json beside the library maps each kernel's
+mangled name to a hash of its gfx950 machine code (the key of measured byte counts).
 """
 from __future__ import annotations
 
@@ -48,6 +49,83 @@ def _compile(src: str) -> str:
     return obj
 
 
+CODE_MAP = os.path.join(PKG, "kernel_code.json")
+
+
+def _llvm(tool: str) -> str:
+    for d in ("/opt/rocm/lib/llvm/bin", "/opt/rocm/llvm/bin"):
+        if os.path.exists(os.path.join(d, tool)):
+            return os.path.join(d, tool)
+    found = shutil.which(tool)
+    if not found:
+        raise RuntimeError("%s not found (ROCm LLVM tools expected under /opt/rocm)" % tool)
+    return found
+
+
+def _code_objects(lib: str) -> list[bytes]:
+    """The gfx950 code objects in the library's .hip_fatbin section: one offload bundle per
+    translation unit (magic, entry count, then offset/size/triple per entry)."""
+    import struct
+    import tempfile
+    with tempfile.TemporaryDirectory() as td:
+        sec = os.path.join(td, "fatbin")
+        subprocess.run([_llvm("llvm-objcopy"), "--dump-section", ".hip_fatbin=" + sec, lib, os.devnull], check=True)
+        data = open(sec, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out, pos = [], data.find(magic)
+    while pos >= 0:
+        n = struct.unpack_from("<Q", data, pos + len(magic))[0]
+        q = pos + len(magic) + 8
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", data, q)
+            triple = data[q + 24:q + 24 + tlen].decode()
+            q += 24 + tlen
+            if triple.endswith(ARCH) or ("--" + ARCH) in triple:
+                out.append(data[pos + off:pos + off + size])
+        pos = data.find(magic, pos + 1)
+    return out
+
+
+def kernel_code_hashes(lib: str = LIB) -> dict:
+    """Mangled kernel name -> SHA-256 of its machine code, over every gfx950 code object in the
+    library. A measurement keyed by this hash (profiles/traffic.json) goes stale exactly when
+    that kernel's code changes."""
+    import hashlib
+    import tempfile
+    res = {}
+    for co in _code_objects(lib):
+        with tempfile.NamedTemporaryFile(suffix=".co") as f:
+            f.write(co)
+            f.flush()
+            secs = subprocess.run([_llvm("llvm-readelf"), "-S", "-W", f.name], capture_output=True, text=True,
+                                  check=True).stdout
+            syms = subprocess.run([_llvm("llvm-readelf"), "-s", "-W", f.name], capture_output=True, text=True,
+                                  check=True).stdout
+        text = None
+        for line in secs.splitlines():
+            parts = line.replace("[ ", "[").split()
+            if len(parts) > 6 and parts[1] == ".text":
+                text = (int(parts[3], 16), int(parts[4], 16))   # address, file offset
+        if text is None:
+            continue
+        for line in syms.splitlines():
+            parts = line.split()
+            if len(parts) >= 8 and parts[3] == "FUNC" and parts[7].startswith("_Z"):
+                addr, size = int(parts[1], 16), int(parts[2])
+                start = text[1] + addr - text[0]
+                res[parts[7]] = hashlib.sha256(co[start:start + size]).hexdigest()
+    # the demangled names too (the form profilers report), when a demangler is installed
+    demangler = shutil.which("llvm-cxxfilt") or shutil.which("c++filt")
+    if demangler:
+        names = sorted(res)
+        dem = subprocess.run([demangler], input="\n".join(names), capture_output=True, text=True,
+                             check=True).stdout.splitlines()
+        for m, d in zip(names, dem):
+            if d != m:
+                res[d] = res[m]
+    return res
+
+
 def build(jobs: int | None = None, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -58,6 +136,10 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    import json
+    with open(CODE_MAP + ".tmp", "w") as f:
+        json.dump(kernel_code_hashes(LIB), f, indent=0, sort_keys=True)
+    os.replace(CODE_MAP + ".tmp", CODE_MAP)
     if verbose:
         print("built", LIB)
     return LIB

@@ -277,6 +277,20 @@ skinny_status skinny_config_resources(const skinny_config *cfg, skinny_resources
     return SKINNY_OK;
 }
 
+skinny_status skinny_config_kernel_name(const skinny_config *cfg, char *buf, int32_t len) {
+    if (!cfg || !buf || len <= 0) return SKINNY_EINVAL;
+    const skinny::KernelEntry *e = skinny::find_entry(*cfg, cfg->m_tile > 0 ? cfg->m_tile : 1);
+    if (!e) return SKINNY_ENOTSUP;
+    const char *name = hipKernelNameRefByPtr(e->fn_bf16, nullptr);
+    if (!name) {
+        skinny::g_last_hip_error = (int32_t)hipErrorInvalidDeviceFunction;
+        return SKINNY_EHIP;
+    }
+    if ((int64_t)strlen(name) >= len) return SKINNY_EINVAL;
+    memcpy(buf, name, strlen(name) + 1);
+    return SKINNY_OK;
+}
+
 const char *skinny_status_string(skinny_status s) {
     switch (s) {
         case SKINNY_OK: return "ok";

@@ -328,5 +328,22 @@ def config_resources(config) -> dict:
     return {f: int(getattr(r, f)) for f, _ in SkinnyResources._fields_}
 
 
+def config_kernel(config) -> dict:
+    """The kernel a plain call with this configuration launches at the tuned shape: its name as
+    the HIP runtime reports it and the hash of its machine code in this build (kernel_code.json,
+    written by the build); None for the hash when the build's map lacks the name."""
+    import json
+    import os
+    c = _as_config(config)
+    buf = ctypes.create_string_buffer(4096)
+    check(lib().skinny_config_kernel_name(ctypes.byref(c), buf, len(buf)), "skinny_config_kernel_name")
+    name = buf.value.decode()
+    try:
+        code = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "kernel_code.json")))
+    except (OSError, ValueError):
+        code = {}
+    return {"name": name, "code_sha256": code.get(name)}
+
+
 def version() -> str:
     return lib().skinny_version().decode()

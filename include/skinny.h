@@ -103,6 +103,16 @@ typedef struct skinny_config {
                                   every other path */
 } skinny_config;
 
+/*
+ * The name of the kernel (the instance whose epilogue writes a plain bf16 [M, N] output, for a
+ * K that needs no ragged-tail handling: what skinny_addmm_bf16 launches with this
+ * configuration at the tuned shape) as the HIP runtime reports it, copied with its
+ * terminating NUL into buf (len bytes). Lets measurements made under a profiler be matched to
+ * a configuration. SKINNY_ENOTSUP if the configuration is not built, SKINNY_EINVAL if buf is
+ * too short, SKINNY_EHIP if the runtime has no name for it.
+ */
+SKINNY_API skinny_status skinny_config_kernel_name(const skinny_config *cfg, char *buf, int32_t len);
+
 /* Register and scratch use of one built configuration (hipFuncGetAttributes). */
 typedef struct skinny_resources {
     int32_t num_vgprs;         /* registers per lane reported by the runtime */

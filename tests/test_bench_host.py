@@ -47,3 +47,24 @@ def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert p.returncode == 2 and "one GPU only" in p.stderr
+
+
+def test_traffic_lookup_is_keyed_by_kernel_code():
+    """A measured byte count applies only to the kernel instance and machine code it was taken
+    on: the committed M = 4 entry resolves for its kernel and hash, and reads None for another
+    hash (a rebuilt kernel), another kernel, or another shape."""
+    entries = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["entries"]
+    e = [x for x in entries if x["M"] == 4][0]
+
+    class FakeLib:
+        def __init__(self, name, code):
+            self.k = {"name": name, "code_sha256": code}
+
+        def config_kernel(self, cfg):
+            return self.k
+    t = bench.lookup_traffic(FakeLib(e["kernel_mangled"], e["code_sha256"]), {}, 4)
+    assert t["bytes"] == e["traffic_bytes"] == e["fetch_bytes"] + e["write_bytes"]
+    assert bench.lookup_traffic(FakeLib(e["kernel"], e["code_sha256"]), {}, 4)["bytes"] == e["traffic_bytes"]
+    assert bench.lookup_traffic(FakeLib(e["kernel_mangled"], "0" * 64), {}, 4) is None
+    assert bench.lookup_traffic(FakeLib("other", e["code_sha256"]), {}, 4) is None
+    assert bench.lookup_traffic(FakeLib(e["kernel_mangled"], e["code_sha256"]), {}, 5) is None
