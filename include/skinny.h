@@ -240,8 +240,22 @@ SKINNY_API skinny_status skinny_kbit_gemv_bf16_acc_f32(const void *X, const uint
  *          ring_v[., hv, t, :] = v_t, ring_k[., h, t, :] = k_t (bf16 conv outputs, before the
  *          norm), ring_g[., hv, t, :] = g[t], ring_beta[., hv, t] = beta_t.
  *   ssm and conv_pool are read only (the verify step commits no state).
- * Which of these readings are the page's and which are taken where it is silent is listed
- * with the oracle that defines them (oracle/kda.c).
+ * What comes from that page and what is a reading where it is silent: the page gives the
+ * calls, argument names, tensor shapes and dtypes (and sizes the ring at 2T positions); it
+ * does not print the kernels' arithmetic. Taken as the plain meaning of an argument name or
+ * the standard definition of the named operation:
+ *   - the conv window is the 3 cached inputs, oldest first, then the T tokens; its output is
+ *     materialised in bf16 (the page's tensors are bf16) before the q | k | v split;
+ *   - the gate is the standard KDA gate (is_kda, no lower bound): softplus with beta 1 and
+ *     threshold 20, scaled by -exp(A_log); beta is the sigmoid of b;
+ *   - the L2 norm adds its 1e-6 inside the square root; q is then multiplied by scale (the
+ *     page passes K^-0.5); value head hv reads q/k head hv / (HV / H);
+ *   - the delta rule decays S per K channel, then u = beta (v - S k^), S += u k^T, o = S q^
+ *     (the output is read after the update);
+ *   - a verify step writes no state: ssm and conv_pool are read only;
+ *   - where in the ring a verify starts is not on the page; token t goes to position t;
+ *   - not built: the page's lower-bound ("safe") gate and parent-token retrieval, whose
+ *     arithmetic the page does not give.
  *
  * Layouts (row-major, device pointers, all bf16 unless noted):
  *   mixed [B*T, dim], dim = 2*H*K + HV*V;  conv_w [dim, 4];  conv_b [dim];
