@@ -241,9 +241,11 @@ struct KbitShape {
 };
 
 // Rows per row group r and workgroup size T (a multiple of 64 holding r * BPR owner lanes and
-// 16 writer lanes per row): the fewest idle SIMD lanes first (waves are counted in rounds of
-// four, one per SIMD), then a size of 256..512 lanes, then the smaller size. G row groups per workgroup so that every local row has a writer group, the
-// partial sums fit their LDS budget and the grid still covers the chip.
+// 16 writer lanes per row): the fewest idle lanes in the launched waves first, then a size of
+// 256..512 lanes, then the smaller size (at K = 3584, BPR = 112: r = 4 and 448 threads, no idle
+// lane; 2 rows in 256 threads leave 32 idle and measured 2-3 % slower). G row groups per
+// workgroup so that every local row has a writer group, the partial sums fit their LDS budget
+// and the grid still covers the chip.
 KbitShape kbit_shape(int64_t N, int64_t K, int MT) {
     const int BPR = (int)(K / 32);
     KbitShape s{16, 256, 1, 0};
@@ -252,10 +254,7 @@ KbitShape kbit_shape(int64_t N, int64_t K, int MT) {
         int best_pen = 2;
         for (int r = 1; r * BPR <= kMaxThreads && 16 * r <= kMaxThreads; ++r) {
             const int T = ((std::max(r * BPR, 16 * r) + 63) / 64) * 64;
-            // a CU runs a workgroup's waves on its 4 SIMDs: T / 64 waves take the time of a
-            // multiple of 4 of them, so count lanes against whole rounds of 4 waves
-            const int slots = ((T / 64 + 3) / 4) * 4 * 64;
-            const double eff = (double)(r * BPR) / slots;
+            const double eff = (double)(r * BPR) / T;
             const int pen = (T >= 256 && T <= 512) ? 0 : 1;
             const bool better = eff > best_eff + 1e-9 ||
                                 (eff > best_eff - 1e-9 && (pen < best_pen || (pen == best_pen && T < s.T)));
