@@ -767,9 +767,12 @@ def run_kda(args, sk):
     from decode_skinny_addmm_amd import synth
     T, H, HV, K, V = 4, 8, 8, 128, 128
     Bs = [int(x) for x in args.ms.split(",")] if args.ms else [1, 4, 16, 64]
+    layouts = args.layouts.split(",")
+    if not layouts or any(lay not in ("snapshots", "ring") for lay in layouts):
+        raise SystemExit("--layouts takes a comma-separated list of snapshots and ring")
     out = open(args.out, "a") if args.out else None
     for B in Bs:
-        for ring in (False, True):
+        for ring in [lay == "ring" for lay in layouts]:
             base = synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V)
             per_copy = B * HV * V * K * 4 * (1 if ring else 1 + T)
             copies = max(2, min(256, -(-320_000_000 // per_copy)))
@@ -846,6 +849,8 @@ def main():
     p.add_argument("--shards", type=int, default=8, help="shard/shard-sweep: ranks the 7168 columns split over")
     p.add_argument("--rank", type=int, default=3, help="shard/shard-sweep: which rank's column block")
     p.add_argument("--kbits", type=str, default="2,3,4,5", help="kbit: comma-separated bits per weight")
+    p.add_argument("--layouts", type=str, default="snapshots,ring",
+                   help="kda: comma-separated state layouts to time (snapshots, ring)")
     p.add_argument("--out", type=str, default=None)
     p.add_argument("--resume", action="store_true",
                    help="sweep/mcurve: skip the (M, N, K, config) rows already valid in --out")

@@ -29,12 +29,24 @@ constexpr int KD = 128;        // head dimension of q and k (the page's shape)
 constexpr int TLIM = 16;       // most draft tokens per verify
 constexpr int CPL = KD / 16;   // K channels per lane
 
+// K channel c (0..7) of lane j of a 16-lane group: two runs of four, at 4j and at 64 + 4j, so a
+// group's 16-byte accesses to a 512-byte state row cover whole 128-byte lines (two per access)
+__device__ __forceinline__ int lch(int j, int c) { return (c >> 2) * (KD / 2) + 4 * j + (c & 3); }
+
 __device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // ror 8
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // ror 4
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // ror 2
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // ror 1
     return v;
+}
+
+// 16-byte load marked nontemporal: the states are read once per call, and keeping them out of
+// the caches' retained set leaves room for the snapshot writes (29 against 37 us at B = 64)
+__device__ __forceinline__ float4 ldnt4(const float *p) {
+    typedef float vf4 __attribute__((ext_vector_type(4)));
+    const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -66,18 +78,24 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
     const int T = (int)a.T, H = (int)a.H, HV = (int)a.HV, V = (int)a.V, R = (int)a.ring_len;
     const int group = HV / H, h = hv / group;
     const size_t dim = (size_t)2 * H * KD + (size_t)HV * V;
-    const int cidx = a.cache_idx[b];
-    const int slot = clampi(cidx, 0, (int)a.slots - 1);
-    const int cline = clampi(cidx, 0, (int)a.lines - 1);
-    const int iline = (a.conv_win || a.snap) ? clampi(a.inter_idx[b], 0, (int)a.lines - 1) : 0;
+    // the cache indices, issued first and both at once (the second reads cache_idx again when
+    // no output needs inter_idx), through the vector memory path (an opaque zero offset), and
+    // first used after the loads below that do not depend on them (the asm there): those go out
+    // without waiting for the indices' round trip. (As scalar loads the compiler may wait for
+    // them before the first vector load; measured 0.3-0.5 us slower at B = 1 and 4.)
+    const bool need_iline = a.conv_win || a.snap;
+    const int32_t *iptr = need_iline ? a.inter_idx : a.cache_idx;
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    int cidx = a.cache_idx[b + zero], iraw = iptr[b + zero];
     const bool qk_writer = v0 == 0 && hv % group == 0;   // writes the q/k windows and ring k of head h
     const bool head_writer = v0 == 0;                    // writes ring g and beta of value head hv
     const bool ring = a.ring_v != nullptr;
 
-    // Loads, all issued before the first wait and in the order they are used (the memory
-    // counter is waited on in issue order): this lane's conv inputs, its gate inputs, then the
-    // state rows (the largest part, needed last: its transfer overlaps the conv, the gates and
-    // the first rows of the recurrence).
+    // Loads, in the order they are used (the memory counter is waited on in issue order): this
+    // lane's conv weights and new inputs and its gate inputs (none depends on the cache
+    // indices), the indices, the cached conv inputs, then the state rows (the largest part,
+    // needed last: its transfer overlaps the conv, the gates and the first rows).
     constexpr int NCH = 2 * KD + BV;             // conv channels of this workgroup
     constexpr int CCH = (NCH + NT - 1) / NT;     // ... per lane
     const int gi = tid >> 4, j = tid & 15;
@@ -99,8 +117,6 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
         for (int q = 0; q < 4; ++q) wraw[u][q] = cw[ch * 4 + q];
         braw_c[u] = cb[ch];
 #pragma unroll
-        for (int s2 = 0; s2 < 3; ++s2) seq[u][s2] = pool[((size_t)cline * 3 + s2) * dim + ch];
-#pragma unroll
         for (int t = 0; t < TMAX; ++t) seq[u][3 + t] = mixed[((size_t)b * T + min(t, T - 1)) * dim + ch];
     }
     const uint16_t *ag = static_cast<const uint16_t *>(a.a);
@@ -117,85 +133,100 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
     }
     const uint16_t braw = bg[((size_t)b * T + min(tid, T - 1)) * HV + hv];
     const float alog = a.A_log[hv];
-    asm volatile("" ::: "memory");             // the state loads stay after the inputs above
+    asm volatile("" : "+v"(cidx), "+v"(iraw) : : "memory");   // the indices are first used here
+    const int slot = clampi(cidx, 0, (int)a.slots - 1);
+    const int cline = clampi(cidx, 0, (int)a.lines - 1);
+    const int iline = need_iline ? clampi(iraw, 0, (int)a.lines - 1) : 0;
+#pragma unroll
+    for (int u = 0; u < CCH; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) seq[u][s2] = pool[((size_t)cline * 3 + s2) * dim + chs[u]];
     float4 s4[RPG][2];
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-        const float *srow = a.ssm + (((size_t)slot * HV + hv) * V + v0 + gi * RPG + r) * KD + j * CPL;
-        s4[r][0] = *reinterpret_cast<const float4 *>(srow);
-        s4[r][1] = *reinterpret_cast<const float4 *>(srow + 4);
+        const float *srow = a.ssm + (((size_t)slot * HV + hv) * V + v0 + gi * RPG + r) * KD + 4 * j;
+        s4[r][0] = ldnt4(srow);
+        s4[r][1] = ldnt4(srow + KD / 2);
     }
     const float negA = -fexp(alog);
 
     // conv over the q, k (head h) and v (rows v0 .. v0+BV of head hv) channels: all T outputs
-    // of a channel from its 3 cached and T new inputs
+    // of a channel from its 3 cached and T new inputs. The arithmetic runs on every lane and
+    // token (lanes past the last channel repeat it, tokens past T repeat token T - 1, as their
+    // loads did) and only the writes are guarded; each result is also consumed outside the
+    // guard (the empty asm), so the compiler cannot move the loads into the guarded code, behind
+    // the state loads, where waiting for them would mean waiting for the whole state.
 #pragma unroll
     for (int u = 0; u < CCH; ++u) {
         const int i = tid + u * NT;
-        if (i < NCH) {
-            const size_t ch = chs[u];
-            float w[4];
+        const bool live = i < NCH;
+        const size_t ch = chs[u];
+        float w[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[q] = bf16_bits_to_f32(wraw[u][q]);
-            const float bias = bf16_bits_to_f32(braw_c[u]);
-            const bool write_win = win && (i >= 2 * KD || qk_writer);
+        for (int q = 0; q < 4; ++q) w[q] = bf16_bits_to_f32(wraw[u][q]);
+        const float bias = bf16_bits_to_f32(braw_c[u]);
+        const bool write_win = win && (i >= 2 * KD || qk_writer);
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    float acc = bias;
+        for (int t = 0; t < TMAX; ++t) {
+            float acc = bias;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = fmaf(w[q], bf16_bits_to_f32(seq[u][t + q]), acc);
-                    // silu with the accurate exp and an IEEE division: this value is rounded to bf16
-                    const uint16_t c = f32_to_bf16_rne(acc / (1.0f + expf(-acc)));
-                    const float cf = bf16_bits_to_f32(c);
-                    if (i < KD) {
-                        sq[t][i] = cf;
-                    } else if (i < 2 * KD) {
-                        sk[t][i - KD] = cf;
-                        if (ring && qk_writer)
-                            static_cast<uint16_t *>(a.ring_k)[(((size_t)slot * H + h) * R + t) * KD + (i - KD)] = c;
-                    } else {
-                        sv[t][i - 2 * KD] = cf;
-                        if (ring)
-                            static_cast<uint16_t *>(a.ring_v)[(((size_t)slot * HV + hv) * R + t) * V + v0 + (i - 2 * KD)] = c;
-                    }
-                    if (write_win)
-#pragma unroll
-                        for (int w2 = 0; w2 < 3; ++w2)
-                            win[(((size_t)iline * T + t) * 3 + w2) * dim + ch] = seq[u][t + 1 + w2];
+            for (int q = 0; q < 4; ++q) acc = fmaf(w[q], bf16_bits_to_f32(seq[u][t + q]), acc);
+            // silu with the accurate exp and an IEEE division: this value is rounded to bf16
+            const uint16_t c = f32_to_bf16_rne(acc / (1.0f + expf(-acc)));
+            const float cf = bf16_bits_to_f32(c);
+            asm volatile("" : : "v"(cf));
+            if (live && t < T) {
+                if (i < KD) {
+                    sq[t][i] = cf;
+                } else if (i < 2 * KD) {
+                    sk[t][i - KD] = cf;
+                    if (ring && qk_writer)
+                        static_cast<uint16_t *>(a.ring_k)[(((size_t)slot * H + h) * R + t) * KD + (i - KD)] = c;
+                } else {
+                    sv[t][i - 2 * KD] = cf;
+                    if (ring)
+                        static_cast<uint16_t *>(a.ring_v)[(((size_t)slot * HV + hv) * R + t) * V + v0 + (i - 2 * KD)] = c;
                 }
+                if (write_win)
+#pragma unroll
+                    for (int w2 = 0; w2 < 3; ++w2)
+                        win[(((size_t)iline * T + t) * 3 + w2) * dim + ch] = seq[u][t + 1 + w2];
             }
         }
     }
 
     // gates from the registers loaded above: exp(g) per token and K channel, beta per token
+    // (unconditional arithmetic, guarded writes, as for the conv)
 #pragma unroll
     for (int u = 0; u < GCH; ++u) {
         const int c = tid + u * NT;
-        if (c < KD) {
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    const float g = negA * softplus20(bf16_bits_to_f32(araw[u][t]) + dtb[u]);
-                    seg[t][c] = fexp(g);
-                    if (ring && head_writer) a.ring_g[(((size_t)slot * HV + hv) * R + t) * KD + c] = g;
-                }
+        for (int t = 0; t < TMAX; ++t) {
+            const float g = negA * softplus20(bf16_bits_to_f32(araw[u][t]) + dtb[u]);
+            const float e = fexp(g);
+            asm volatile("" : : "v"(e));
+            if (c < KD && t < T) {
+                seg[t][c] = e;
+                if (ring && head_writer) a.ring_g[(((size_t)slot * HV + hv) * R + t) * KD + c] = g;
             }
         }
     }
-    if (tid < T) {
+    {
         const float beta = 1.0f / (1.0f + fexp(-bf16_bits_to_f32(braw)));
-        sbeta[tid] = beta;
-        if (ring && head_writer) a.ring_beta[((size_t)slot * HV + hv) * R + tid] = beta;
+        asm volatile("" : : "v"(beta));
+        if (tid < T) {
+            sbeta[tid] = beta;
+            if (ring && head_writer) a.ring_beta[((size_t)slot * HV + hv) * R + tid] = beta;
+        }
     }
     __syncthreads();
 
     // L2 norms of q and k per token: one 16-lane group per (token, q|k)
     for (int r = gi; r < 2 * T; r += GR) {
-        const float *src = r < T ? &sq[r][j * CPL] : &sk[r - T][j * CPL];
+        const float *src = r < T ? sq[r] : sk[r - T];
         float p = 0.0f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) p = fmaf(src[c], src[c], p);
+        for (int c = 0; c < CPL; ++c) p = fmaf(src[lch(j, c)], src[lch(j, c)], p);
         p = row16_sum(p);
         if (j == 0) {
             const float n = 1.0f / sqrtf(p + 1e-6f);
@@ -205,9 +236,9 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
     }
     __syncthreads();
 
+    uint16_t *out = static_cast<uint16_t *>(a.out);
     // the recurrence, row by row (all T tokens of a row before the next): each row waits only
     // for its own 512 bytes of state, so the state stream overlaps the arithmetic
-    uint16_t *out = static_cast<uint16_t *>(a.out);
     if constexpr (TMAX == 4) {
         // up to 4 tokens: this lane's exp(g), k^ and q^ slices of every token, beta and the v
         // values of its rows move to registers once; the row pairs below then run on VALU and
@@ -219,9 +250,9 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
             const float kn = skn[tc], qn = sqn[tc];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                e[t][c] = seg[tc][j * CPL + c];
-                kk[t][c] = sk[tc][j * CPL + c] * kn;
-                qq[t][c] = sq[tc][j * CPL + c] * qn;
+                e[t][c] = seg[tc][lch(j, c)];
+                kk[t][c] = sk[tc][lch(j, c)] * kn;
+                qq[t][c] = sq[tc][lch(j, c)] * qn;
             }
             bt[t] = sbeta[tc];
 #pragma unroll
@@ -269,9 +300,9 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
                         const int vl = gi * RPG + r0 + x;
                         if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op[x]);
                         if (a.snap) {
-                            float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
+                            float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + 4 * j;
                             *reinterpret_cast<float4 *>(dst) = make_float4(S[x][0], S[x][1], S[x][2], S[x][3]);
-                            *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[x][4], S[x][5], S[x][6], S[x][7]);
+                            *reinterpret_cast<float4 *>(dst + KD / 2) = make_float4(S[x][4], S[x][5], S[x][6], S[x][7]);
                         }
                     }
                 }
@@ -289,8 +320,8 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
                 float kk[CPL];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
-                    kk[c] = sk[t][j * CPL + c] * kn;
-                    S[c] *= seg[t][j * CPL + c];
+                    kk[c] = sk[t][lch(j, c)] * kn;
+                    S[c] *= seg[t][lch(j, c)];
                     skp = fmaf(S[c], kk[c], skp);
                 }
                 skp = row16_sum(skp);
@@ -300,14 +331,14 @@ __global__ __launch_bounds__(GR * 16) void kda_verify_kernel(skinny_kda_args a) 
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     S[c] = fmaf(u, kk[c], S[c]);
-                    op = fmaf(S[c], sq[t][j * CPL + c] * qn, op);
+                    op = fmaf(S[c], sq[t][lch(j, c)] * qn, op);
                 }
                 op = row16_sum(op);
                 if (j == 0) out[(((size_t)b * T + t) * HV + hv) * V + v0 + vl] = f32_to_bf16_rne(op);
                 if (a.snap) {
-                    float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + j * CPL;
+                    float *dst = a.snap + ((((size_t)iline * T + t) * HV + hv) * V + v0 + vl) * KD + 4 * j;
                     *reinterpret_cast<float4 *>(dst) = make_float4(S[0], S[1], S[2], S[3]);
-                    *reinterpret_cast<float4 *>(dst + 4) = make_float4(S[4], S[5], S[6], S[7]);
+                    *reinterpret_cast<float4 *>(dst + KD / 2) = make_float4(S[4], S[5], S[6], S[7]);
                 }
             }
         }

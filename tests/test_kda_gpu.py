@@ -55,10 +55,12 @@ def midpoint_distance(x):
     return np.abs(frac - 0.5) * np.ldexp(1.0 / 256.0, e)
 
 
-def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True):
+def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True, snapshots=None):
     """One verify call against the oracle. clean: inputs moved away from conv rounding
     midpoints first (clean_inputs), so every allowance below is empty and the bars are the
-    tight ones; otherwise the allowances cover values that fp32 and fp64 may round apart."""
+    tight ones; otherwise the allowances cover values that fp32 and fp64 may round apart.
+    snapshots: defaults to `not ring`; False with ring False asks for o (and windows) only."""
+    snap = (not ring) if snapshots is None else snapshots
     t_inp = synth.make_kda_inputs(B, T=T, H=H, HV=HV, K=K, V=V, seed=seed)
     if permute:
         lines = B + 1
@@ -68,12 +70,12 @@ def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True):
         t_inp = clean_inputs(t_inp, T, H, HV, K, V)
     n_inp = synth.kda_to_numpy(t_inp)
     scale = K ** -0.5
-    print("kda", dict(B=B, T=T, H=H, HV=HV, K=K, V=V, ring=ring, seed=seed), flush=True)
+    print("kda", dict(B=B, T=T, H=H, HV=HV, K=K, V=V, ring=ring, snapshots=snap, seed=seed), flush=True)
     d = {k: v.cuda() for k, v in t_inp.items()}
-    o = sk.kda_verify(d, T, H, HV, K, V, scale, snapshots=not ring, ring=ring)
+    o = sk.kda_verify(d, T, H, HV, K, V, scale, snapshots=snap, ring=ring)
     torch.cuda.synchronize()
-    ref = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=not ring, ring_len=16 if ring else 0)
-    what = "kda B=%d T=%d H=%d HV=%d V=%d ring=%s" % (B, T, H, HV, V, ring)
+    ref = oracle.kda_verify(n_inp, T, H, HV, K, V, scale, snapshots=snap, ring_len=16 if ring else 0)
+    what = "kda B=%d T=%d H=%d HV=%d V=%d ring=%s snapshots=%s" % (B, T, H, HV, V, ring, snap)
     assert np.array_equal(synth.bits(d["win_pool"].cpu()), ref["win_pool"]), what + ": windows"
     dim = 2 * H * K + HV * V
     conv_bits = oracle.round_bf16(ref["conv_exact"])
@@ -93,7 +95,7 @@ def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True):
     og, oe = P.bits_of(o), ref["o_exact"]
     P.check_y(og[~aff], ref["o"][~aff], oe[~aff], what + ": o")
     if aff.any():
-        s_max = float(np.abs(ref["inter_ssm"] if not ring else n_inp["ssm"]).max()) * 4.0
+        s_max = float(np.abs(ref["inter_ssm"] if snap else n_inp["ssm"]).max()) * 4.0
         lim_o = 2.0 ** -5 * scale * np.sqrt(K) * s_max
         assert np.abs(oracle.bf16_bits_to_f64(og[aff]) - oe[aff]).max() <= lim_o, what + ": o near a flip"
     if ring:
@@ -113,7 +115,7 @@ def run_case(sk, B, T, H, HV, K, V, ring, seed=0, permute=True, clean=True):
             assert not (diff[~near_ring[name]] > 0).any(), what + ": %s differs away from a midpoint" % name
         assert np.allclose(d["g"].cpu().numpy(), ref["g"], rtol=1e-5, atol=1e-7), what + ": g"
         assert np.allclose(d["beta"].cpu().numpy(), ref["beta"], rtol=1e-5, atol=1e-7), what + ": beta"
-    else:
+    elif snap:
         S = d["inter_ssm"].cpu().numpy().astype(np.float64)
         Se = ref["inter_ssm"]
         rms = float(np.sqrt(np.mean(Se ** 2)))
@@ -154,12 +156,19 @@ def test_kda_small(sk, B, T, H, HV, V, ring):
 
 
 @pytest.mark.parametrize("ring", [False, True])
-@pytest.mark.parametrize("B", [1, 4, 16, 32])
+@pytest.mark.parametrize("B", [1, 4, 16, 32, 64])
 def test_kda_page_shape(sk, B, ring):
     """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens. The launch takes 16 state rows
-    per workgroup at B = 1 and 4, 32 at B = 16 and 64 at B = 32 (128 at B = 64, in the ring test
-    below)."""
+    per workgroup at B = 1 and 4, 32 at B = 16, 64 at B = 32 and 128 at B = 64."""
     run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
+
+
+@pytest.mark.parametrize("B,T,H,HV,V", [(64, 4, 8, 8, 128), (3, 1, 2, 4, 32), (3, 3, 2, 4, 32), (2, 5, 1, 2, 64),
+                                        (4, 8, 2, 2, 128), (2, 9, 1, 1, 16), (2, 16, 1, 2, 32)])
+def test_kda_outputs_only(sk, B, T, H, HV, V):
+    """Neither snapshots nor ring: only o (and the conv windows) are written; the 4-, 8- and
+    16-token instances of the kernel, against the oracle."""
+    run_case(sk, B, T, H, HV, 128, V, False, snapshots=False)
 
 
 @pytest.mark.parametrize("ring", [False, True])
