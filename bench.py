@@ -106,6 +106,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def config_shard(args, candidates):
+    """Every n-th candidate from the i-th on (--config-shard i --num-config-shards n), so a long
+    sweep can be split over several runs; the shards together cover the list once."""
+    return candidates[args.config_shard::args.num_config_shards]
+
+
 def parse_config(s: str | None):
     if not s:
         return None
@@ -583,12 +589,13 @@ def run_default(args, sk):
 
 def device_meta() -> dict:
     """What the rows are measured on: device name, gfx architecture, CU count, HIP and torch
-    versions, and the host's usable cores (the CPU oracle's baseline runs there)."""
+    versions, the host's usable cores (the CPU oracle's baseline runs there), and the
+    SKINNY_CONFIG override when one replaced the library's table for this run."""
     import torch
     p = torch.cuda.get_device_properties(0)
     return {"device": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
             "cus": p.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
-            "host_cores": len(os.sched_getaffinity(0))}
+            "host_cores": len(os.sched_getaffinity(0)), "skinny_config_env": os.environ.get("SKINNY_CONFIG")}
 
 
 def done_rows(path):
@@ -665,7 +672,8 @@ def run_shard(args, sk):
     for M in Ms:
         wl = ShardWorkload(M, copies, args.shards, args.rank)
         if args.mode == "shard-sweep":
-            configs = [c for c in sk.configs() if -(-M // c["m_tile"]) <= 4 and (not args.paths or c["path"] in paths)]
+            configs = config_shard(args, [c for c in sk.configs()
+                                          if -(-M // c["m_tile"]) <= 4 and (not args.paths or c["path"] in paths)])
         for cfg in (configs or [args.config or sk.select_config(M, N)]):
             def launch(X, W, R, Y, cfg=cfg):
                 return sk.addmm_shard(X, W, R, out=Y, round_product=True, no_neg_zero=True, config=cfg)
@@ -862,9 +870,16 @@ def main():
     p.add_argument("--n", type=int, default=N_DIM, help="sweep/mcurve: N (rows of W); the default run uses 7168")
     p.add_argument("--k", type=int, default=K_DIM, help="sweep/mcurve: K; the default run uses 3584")
     p.add_argument("--paths", type=str, default=None, help="sweep only these kernel paths (comma-separated ids)")
+    p.add_argument("--config-shard", type=int, default=0,
+                   help="sweep/shard-sweep: time candidates i, i + n, i + 2n, ... of each M's list")
+    p.add_argument("--num-config-shards", type=int, default=1,
+                   help="sweep/shard-sweep: n, the number of shards the candidate lists are split into")
     p.add_argument("--with-torch", action="store_true",
                    help="mcurve: add torch.addmm (the vendor library) as a context row")
     args = p.parse_args()
+    if args.num_config_shards < 1 or not 0 <= args.config_shard < args.num_config_shards:
+        print("--config-shard must lie in [0, --num-config-shards)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
@@ -893,8 +908,9 @@ def main():
         paths = {int(x) for x in args.paths.split(",")} if args.paths else None
         # configurations that would re-read W more than 4 times (ceil(M / m_tile) passes) are
         # skipped: they are never competitive and take long to time
-        sweep_rows(args, sk, Ms, lambda m: [c for c in sk.configs()
-                                            if -(-m // c["m_tile"]) <= 4 and (paths is None or c["path"] in paths)])
+        sweep_rows(args, sk, Ms, lambda m: config_shard(args, [c for c in sk.configs()
+                                                               if -(-m // c["m_tile"]) <= 4
+                                                               and (paths is None or c["path"] in paths)]))
     else:
         Ms = [int(x) for x in args.ms.split(",")] if args.ms else (
             [args.m] if args.m else [1, 2, 4, 8, 16, 32, 64, 128, 256])

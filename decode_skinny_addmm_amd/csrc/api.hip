@@ -1,5 +1,7 @@
 // api.hip -- the C ABI of libskinny.so (declared in include/skinny.h): argument checks,
 // configuration lookup and dispatch to the compiled kernel instances.
+#include <errno.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <climits>
@@ -87,6 +89,56 @@ skinny_config select(int64_t M, int64_t N, int64_t K) {
     return M <= 16 ? kFallbackSmall : kFallbackLarge;
 }
 
+// SKINNY_CONFIG: "PATH,BLOCK,OUTPUTS,K_UNROLL,VECTOR_WIDTH[,M_TILE[,K_SPLIT[,K_STAGE]]]", decimal
+// integers, the missing trailing fields 0, 1 and 0. Parsed once per process.
+struct EnvConfig {
+    bool set = false, valid = false;
+    skinny_config cfg{};
+};
+
+EnvConfig parse_env_config() {
+    EnvConfig r;
+    const char *s = getenv("SKINNY_CONFIG");
+    if (!s) return r;
+    r.set = true;
+    int64_t v[8];
+    int n = 0;
+    const char *p = s;
+    for (;;) {
+        char *end = nullptr;
+        errno = 0;
+        const long long x = strtoll(p, &end, 10);
+        if (end == p || errno != 0 || x < INT32_MIN || x > INT32_MAX || n == 8) return r;
+        v[n++] = x;
+        while (*end == ' ') ++end;
+        if (*end == '\0') break;
+        if (*end != ',') return r;
+        p = end + 1;
+    }
+    if (n < 5) return r;
+    r.cfg = skinny_config{(int32_t)v[0], (int32_t)v[1], (int32_t)v[2], (int32_t)v[3], (int32_t)v[4],
+                          n > 5 ? (int32_t)v[5] : 0, n > 6 ? (int32_t)v[6] : 1, n > 7 ? (int32_t)v[7] : 0};
+    r.valid = true;
+    return r;
+}
+
+const EnvConfig &env_config() {
+    static const EnvConfig e = parse_env_config();
+    return e;
+}
+
+// The configuration of a call that names none: SKINNY_CONFIG when set, else the table.
+skinny_status default_config(int64_t M, int64_t N, int64_t K, skinny_config *out) {
+    const EnvConfig &e = env_config();
+    if (e.set) {
+        if (!e.valid) return SKINNY_EINVAL;
+        *out = e.cfg;
+        return SKINNY_OK;
+    }
+    *out = select(M, N, K);
+    return SKINNY_OK;
+}
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr uint32_t kKnownFlags = SKINNY_FLAG_ROUND_PRODUCT | SKINNY_FLAG_NO_NEG_ZERO;
@@ -108,7 +160,13 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
         return SKINNY_EALIGN;
     // kernel index arithmetic is 32-bit for sizes, 64-bit for offsets
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX || ldr > INT_MAX || ldo > INT_MAX) return SKINNY_ENOTSUP;
-    const skinny_config c = cfg ? *cfg : select(M, N, K);
+    skinny_config c;
+    if (cfg) {
+        c = *cfg;
+    } else {
+        const skinny_status st = default_config(M, N, K, &c);
+        if (st != SKINNY_OK) return st;
+    }
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
         c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0 ||
@@ -248,8 +306,7 @@ skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const void *W, cons
 
 skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out) {
     if (!out || M < 0 || N < 0 || K < 0) return SKINNY_EINVAL;
-    *out = skinny::select(M, N, K);
-    return SKINNY_OK;
+    return skinny::default_config(M, N, K, out);
 }
 
 int32_t skinny_num_configs(void) { return (int32_t)skinny::registry().all.size(); }

@@ -131,6 +131,15 @@ SKINNY_API skinny_status skinny_addmm_bf16(const void *X, const void *W, const v
  * The tuned configuration for a problem size (an M-indexed table measured on MI355X; the
  * page-1 benchmark's per-M "residual_config" lookup plays the same role). Host-only, no
  * HIP call. Returns SKINNY_EINVAL for a NULL `out` or negative sizes.
+ *
+ * Override for sweeps and experiments: if the environment variable SKINNY_CONFIG is set when
+ * the library first needs a configuration, its value replaces the table for the whole process,
+ * here and in every call that passes no configuration (skinny_addmm_bf16, and the calls below
+ * with cfg == NULL). The value is 5 to 8 comma-separated decimal integers,
+ * PATH,BLOCK,OUTPUTS,K_UNROLL,VECTOR_WIDTH[,M_TILE[,K_SPLIT[,K_STAGE]]] (the skinny_config
+ * fields in order; missing trailing fields are 0, 1 and 0). A malformed value makes those calls
+ * return SKINNY_EINVAL; a configuration that is not built, or does not take the shape, makes
+ * the compute calls return SKINNY_ENOTSUP, as an explicit one would. It is read once.
  */
 SKINNY_API skinny_status skinny_select_config(int64_t M, int64_t N, int64_t K, skinny_config *out);
 

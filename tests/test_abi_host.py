@@ -73,6 +73,62 @@ def test_table_rows_resolve_without_fallback(L, N):
         assert c.as_dict()["path"] not in (1, 3), (M, N, c.as_dict())
 
 
+ENV_PROBE = r"""
+import ctypes, json, sys
+sys.path.insert(0, sys.argv[1])
+from decode_skinny_addmm_amd import _lib
+L = _lib.lib()
+c = _lib.SkinnyConfig()
+sel = L.skinny_select_config(4, 7168, 3584, ctypes.byref(c))
+built = []
+for i in range(L.skinny_num_configs()):
+    b = _lib.SkinnyConfig()
+    L.skinny_get_config(i, ctypes.byref(b))
+    built.append(list(b.as_dict().values()))
+call = None
+if sys.argv[2] == "call":
+    # only for values that fail before any launch (malformed, or not built): the pointers are fake
+    assert sel != 0 or list(c.as_dict().values()) not in built
+    fake = ctypes.c_void_p(4096)
+    call = L.skinny_addmm_bf16(fake, fake, fake, fake, 1, 64, 64, None)
+print(json.dumps({"sel": sel, "cfg": list(c.as_dict().values()), "call": call}))
+"""
+
+
+def run_env_probe(value, mode):
+    import json
+    import subprocess
+    import sys
+    env = dict(os.environ, SKINNY_CONFIG=value)
+    out = subprocess.run([sys.executable, "-c", ENV_PROBE, ROOT, mode], env=env, capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    return json.loads(out.stdout.strip().splitlines()[-1])
+
+
+@pytest.mark.parametrize("value,cfg", [
+    ("2, 256, 32, 4, 8, 4", [2, 256, 32, 4, 8, 4, 1, 0]),           # trailing fields default to 1, 0
+    ("6,512,64,4,8,128,2,64", [6, 512, 64, 4, 8, 128, 2, 64]),
+    ("0,448,4,7,8", [0, 448, 4, 7, 8, 0, 1, 0])])
+def test_env_config_replaces_the_table(L, value, cfg):
+    """SKINNY_CONFIG replaces the table for calls that name no configuration (read once per
+    process, so each case runs in a child process)."""
+    r = run_env_probe(value, "select")
+    assert r["sel"] == 0 and r["cfg"] == cfg
+
+
+@pytest.mark.parametrize("value,sel,call", [
+    ("2,256,32,4", 1, 1),             # too few fields
+    ("2,256,32,4,8,4,1,0,9", 1, 1),   # too many
+    ("2,256,x,4,8", 1, 1),            # not a number
+    ("2,256,32,4,8,", 1, 1),          # empty field
+    ("2;256;32;4;8", 1, 1),           # wrong separator
+    ("0,64,1,1,8", 0, 3)])            # well formed but not built: the compute call says so
+def test_env_config_errors(L, value, sel, call):
+    r = run_env_probe(value, "call")
+    assert r["sel"] == sel and r["call"] == call
+
+
 def test_get_config_range(L):
     c = _lib.SkinnyConfig()
     assert L.skinny_get_config(-1, ctypes.byref(c)) == 1

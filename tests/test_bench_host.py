@@ -1,4 +1,5 @@
-"""Host-side pieces of bench.py (CPU only): byte counts, sweep resume, the one-GPU guard."""
+"""Host-side pieces of bench.py (CPU only): byte counts, sweep resume and sharding, the one-GPU
+guard."""
 import json
 import os
 import subprocess
@@ -68,3 +69,20 @@ def test_traffic_lookup_is_keyed_by_kernel_code():
     assert bench.lookup_traffic(FakeLib(e["kernel_mangled"], "0" * 64), {}, 4) is None
     assert bench.lookup_traffic(FakeLib("other", e["code_sha256"]), {}, 4) is None
     assert bench.lookup_traffic(FakeLib(e["kernel_mangled"], e["code_sha256"]), {}, 5) is None
+
+
+def test_config_shards_cover_the_candidates_once():
+    import types
+    cands = [{"i": i} for i in range(23)]
+    for n in (1, 2, 3, 7):
+        parts = [bench.config_shard(types.SimpleNamespace(config_shard=i, num_config_shards=n), cands)
+                 for i in range(n)]
+        seen = sorted(c["i"] for p in parts for c in p)
+        assert seen == list(range(23))
+        assert max(map(len, parts)) - min(map(len, parts)) <= 1
+
+
+def test_bad_config_shard_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mode", "sweep", "--config-shard", "2",
+                        "--num-config-shards", "2"], capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2 and "--config-shard" in p.stderr
