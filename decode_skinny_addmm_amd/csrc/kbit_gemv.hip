@@ -99,6 +99,56 @@ __device__ __forceinline__ void block_dot(const uint32_t (&P)[KB], uint32_t a, c
     for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
 }
 
+// k = 2 and 4: the same partial sum with two indices per lookup. Word c' (c' in [0, 8) with
+// c' mod 2k < k) of each half of the block collects the elements e, e + k, e + 16, e + 16 + k
+// (e = c' in the low half, c' + 8 in the high half; the words cover all 32 elements): plane i is
+// rotated once per half so that element j's bit lands at j + 3 + i (low) or j - 5 + i (high),
+// and one AND-OR per plane with the mask of positions c' + 3 + i + {0, k, 16, 16 + k} leaves
+// index(e) + index(e + k) << k at bits c' + 3 ... and index(e + 16) + index(e + 16 + k) << k at
+// bits c' + 19 ..., each field 3 + 2k bits long with its low 3 bits clear: one bit-field extract
+// gives the byte address of a float2 (codebook[a], codebook[b]) in a 2^(2k)-entry LDS table.
+// Per 4 weights: k + 2 VALU instructions and two 8-byte lookups (the byte form: k + 5 and four).
+template <int KB, int MT>
+__device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t a, const float (&x)[MT][32],
+                                               const uint32_t (&pm)[7], const char *pairb, float (&out)[MT]) {
+    constexpr int FW = 3 + 2 * KB;                     // field width in bits
+    uint32_t Qlo[KB], Qhi[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        Qlo[i] = rotr(P[i], 29 - i);                   // element j -> bit j + 3 + i
+        Qhi[i] = rotr(P[i], 5 - i);                    // element j -> bit j - 5 + i (mod 32)
+    }
+    float s[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s[m] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int cp = 0; cp < 8; ++cp) {
+            if (cp % (2 * KB) >= KB) continue;
+            const uint32_t(&Q)[KB] = h ? Qhi : Qlo;
+            uint32_t w = Q[0] & pm[cp];
+#pragma unroll
+            for (int i = 1; i < KB; ++i) w = and_or(Q[i], pm[cp + i], w);
+            const uint32_t f0 = __builtin_amdgcn_ubfe(w, cp, FW);
+            const uint32_t f1 = __builtin_amdgcn_ubfe(w, cp + 16, FW);
+            const float2 v0 = *reinterpret_cast<const float2 *>(pairb + f0);
+            const float2 v1 = *reinterpret_cast<const float2 *>(pairb + f1);
+            const int e = cp + 8 * h;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                s[m] = fmaf(x[m][e], v0.x, s[m]);
+                s[m] = fmaf(x[m][e + KB], v0.y, s[m]);
+                s[m] = fmaf(x[m][e + 16], v1.x, s[m]);
+                s[m] = fmaf(x[m][e + 16 + KB], v1.y, s[m]);
+            }
+        }
+    }
+    const float scale = e4m4_decode(a);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
+}
+
 // One launch: grid.x = ceil(N / (r * G)), grid.y = ceil(M / MT); blockDim.x = T (a multiple of
 // 64 with r * BPR <= T and r * G <= T / 16); K >= 32. Lane t < r * BPR owns row offset t / BPR and
 // block t % BPR; the other lanes compute a clamped copy that is not stored, and help with the
@@ -111,7 +161,9 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
                                                                 const uint16_t *R, void *out, int M, int N, int K,
                                                                 int r, int G) {
     constexpr int L = 1 << KB;
+    constexpr bool PAIR = KB == 2 || KB == 4;   // two indices per lookup (block_dot_pair)
     __shared__ float cbs[L];
+    __shared__ float2 pairs[PAIR ? L * L : 1];
     extern __shared__ float part[];        // [r * G][MT][BPR]
 
     const int tid = threadIdx.x;
@@ -160,6 +212,19 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
     // the loads above, so that its wait counts only the codebook load
     asm volatile("" : "+v"(cbv) :: "memory");
     if (lane < L) cbs[lane] = cbv;
+    if constexpr (PAIR) {
+        // the pair table, also per wave: entry a + (b << k) = (codebook[a], codebook[b]), read
+        // from this wave's own codebook writes above (a wave's LDS operations run in order)
+#pragma unroll
+        for (int e0 = 0; e0 < L * L; e0 += 64)
+            if (e0 + lane < L * L) pairs[e0 + lane] = make_float2(cbs[(e0 + lane) & (L - 1)], cbs[(e0 + lane) >> KB]);
+    }
+    uint32_t pm[7];                              // pair masks: positions s + 3 + {0, k, 16, 16 + k}
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        pm[j] = rotl_c((1u | (1u << KB) | (1u << 16) | (1u << (16 + KB))) << 3, j);
+        asm("" : "+v"(pm[j]));
+    }
     uint32_t msk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -182,6 +247,7 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
         }
 
     const char *cbb = reinterpret_cast<const char *>(cbs);
+    const char *pairb = reinterpret_cast<const char *>(pairs);
     // two row groups per step, so that their lookups and FMAs interleave; the empty asm
     // pins each group's words to its step, so that the compiler cannot hoist their decode
     // (and the wait for their loads) above the barrier and the groups before
@@ -192,8 +258,13 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
         asm volatile("" : "+v"(A[g]), "+v"(A[g + 1]));
         if (g + 1 < G) {
             float o0[MT], o1[MT];
-            block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
-            block_dot<KB, MT>(P[g + 1], A[g + 1], x, msk, cbb, o1);
+            if constexpr (PAIR) {
+                block_dot_pair<KB, MT>(P[g], A[g], x, pm, pairb, o0);
+                block_dot_pair<KB, MT>(P[g + 1], A[g + 1], x, pm, pairb, o1);
+            } else {
+                block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
+                block_dot<KB, MT>(P[g + 1], A[g + 1], x, msk, cbb, o1);
+            }
             if (active) {
                 float *p0 = part + (size_t)(g * r + roff) * MT * BPR + blk;
                 float *p1 = p0 + (size_t)r * MT * BPR;
@@ -205,7 +276,8 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
             }
         } else if (g < G) {
             float o0[MT];
-            block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
+            if constexpr (PAIR) block_dot_pair<KB, MT>(P[g], A[g], x, pm, pairb, o0);
+            else block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
             if (active) {
                 float *p0 = part + (size_t)(g * r + roff) * MT * BPR + blk;
 #pragma unroll
