@@ -362,13 +362,15 @@ hipError_t launch_shape(const skinny_kda_args &a, hipStream_t stream) {
 
 hipError_t launch_kda_verify(const skinny_kda_args &a, hipStream_t stream) {
     // Rows per workgroup: the conv of the q/k channels and the gates are recomputed by every
-    // workgroup of a (batch row, value head), so take the most rows that still leave >= 512
-    // workgroups (2 per CU), and never fewer than 16: at B = 1 (64 workgroups of 16 rows) that
-    // is faster than 256 workgroups of 4 rows, whose conv work is 4 times larger.
+    // workgroup of a (batch row, value head), so rows per workgroup are as many as still fill the
+    // chip: 128 while that gives >= 512 workgroups (two per CU), else the most of 64, 32, 16 that
+    // gives >= 256 (measured at B = 1 ... 64 in both layouts: within 1 % of the best forced shape
+    // everywhere; one ">= 512" threshold for every size loses 5-10 % at B = 8 and 16), and
+    // never fewer than 16 (at B = 1, 64 workgroups of 16 rows beat 256 of 4).
     const int64_t rows = a.B * a.HV * a.V;
     if (a.V % 128 == 0 && rows / 128 >= 512) return launch_shape<16, 8>(a, stream);
-    if (a.V % 64 == 0 && rows / 64 >= 512) return launch_shape<16, 4>(a, stream);
-    if (a.V % 32 == 0 && rows / 32 >= 512) return launch_shape<16, 2>(a, stream);
+    if (a.V % 64 == 0 && rows / 64 >= 256) return launch_shape<16, 4>(a, stream);
+    if (a.V % 32 == 0 && rows / 32 >= 256) return launch_shape<16, 2>(a, stream);
     return launch_shape<16, 1>(a, stream);
 }
 

@@ -156,10 +156,10 @@ def test_kda_small(sk, B, T, H, HV, V, ring):
 
 
 @pytest.mark.parametrize("ring", [False, True])
-@pytest.mark.parametrize("B", [1, 4, 16, 32, 64])
+@pytest.mark.parametrize("B", [1, 4, 8, 16, 32, 64])
 def test_kda_page_shape(sk, B, ring):
     """The page's layer: H = HV = 8, K = V = 128, 4 draft tokens. The launch takes 16 state rows
-    per workgroup at B = 1 and 4, 32 at B = 16, 64 at B = 32 and 128 at B = 64."""
+    per workgroup at B = 1 and 4, 32 at B = 8, 64 at B = 16 and 32 and 128 at B = 64."""
     run_case(sk, B, 4, 8, 8, 128, 128, ring, permute=B > 1)
 
 
