@@ -18,7 +18,9 @@
 //     c, c+8, c+16, c+24 into one word whose bytes are the four indices times 4, i.e. the
 //     LDS byte addresses of their codebook entries; one rotation re-aligns the word; one
 //     bit-field extract per element feeds a ds_read_b32 (the 2^k-entry fp32 table spans at
-//     most 32 banks, so every lookup is conflict-free);
+//     most 32 banks, so every lookup is conflict-free). For k = 2 and 4 the words instead
+//     hold two indices per field, and one ds_read_b64 fetches both codebook values from a
+//     table of pairs (block_dot_pair);
 //   * one fp32 FMA per weight and row; the block's sum is scaled once by its decoded absmax;
 //   * per-block partial sums meet in LDS; 16 lanes per output row add them and write
 //     bf16(sum + R) with one rounding (R is loaded by the writing lane at kernel start).

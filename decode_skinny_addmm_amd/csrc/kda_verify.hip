@@ -10,12 +10,14 @@
 // at V = K = 128) and, in snapshot mode, written T times; everything else (the conv inputs
 // of 2K + V channels, the gates) is a few KB. So the kernel is an HBM stream of states, and
 // the layout is chosen for it:
-//   * a workgroup owns BV rows of one state; 16 lanes per row, 8 consecutive K channels per
-//     lane: the state slice lives in registers for all T tokens, every load and snapshot store
-//     is a 16-byte vector and a row is 512 contiguous bytes;
-//   * the state load is issued first, so that its latency hides behind the conv and gate
-//     work; conv outputs (rounded to bf16, the precision the unfused path materialises),
-//     the normalised q and k, exp(g) and beta of all T tokens are staged in LDS once;
+//   * a workgroup owns BV rows of one state; 16 lanes per row, 8 K channels per lane in two
+//     runs of four (lch): the state slice lives in registers for all T tokens, every load and
+//     snapshot store is a 16-byte vector, and a 16-lane group's access covers whole 128-byte
+//     lines of the row's 512 contiguous bytes; the state loads are nontemporal;
+//   * the state loads are issued right after the conv and gate inputs, so that their latency
+//     hides behind the conv and gate work, which never waits for them; conv outputs (rounded
+//     to bf16, the precision the unfused path materialises), the normalised q and k, exp(g)
+//     and beta of all T tokens are staged in LDS once;
 //   * per token: decay, S k^ and S q^ as 8-wide partial dots closed by a 16-lane DPP sum;
 //   * the conv over q/k channels is recomputed by every workgroup of the head (256 channels
 //     x T tokens, a few hundred FMAs per lane) instead of a second kernel and a round trip;
