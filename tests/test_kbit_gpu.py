@@ -109,24 +109,28 @@ def test_kbit_k_zero_is_residual(sk):
     assert torch.equal(Y.cpu().view(torch.int16), R.cpu().view(torch.int16))
 
 
+@pytest.mark.parametrize("kb", [3, 4])
 @pytest.mark.parametrize("M,K", [(2, 16384), (1, 14336), (4, 8192)])
-def test_kbit_long_rows(sk, M, K):
-    """Long rows: one lane per block up to 512 blocks, a row group of one row per workgroup."""
-    X, ps, As, rs, cb = synth.make_kbit_inputs(M, 48, K, kbits=3, seed=K)
-    Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, 3, rs[0])
-    Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), 3, synth.bits(rs[0]))
-    P.check_y(Yg, Yo, Ao, "kbit long K=%d" % K)
-    P.check_acc(Ag, Ao, "kbit long K=%d" % K)
+def test_kbit_long_rows(sk, kb, M, K):
+    """Long rows: one lane per block up to 512 blocks, a row group of one row per workgroup;
+    k = 3 takes the one-index-per-lookup decode, k = 4 the pair table."""
+    X, ps, As, rs, cb = synth.make_kbit_inputs(M, 48, K, kbits=kb, seed=K + kb)
+    Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, kb, rs[0])
+    Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), kb, synth.bits(rs[0]))
+    P.check_y(Yg, Yo, Ao, "kbit %d long K=%d" % (kb, K))
+    P.check_acc(Ag, Ao, "kbit %d long K=%d" % (kb, K))
 
 
-def test_kbit_poisoned_output_fully_written(sk):
-    """Every output is written: Y starts as NaN (bf16 and fp32 entry) and must hold none after."""
+@pytest.mark.parametrize("kb", [3, 4])
+def test_kbit_poisoned_output_fully_written(sk, kb):
+    """Every output is written: Y starts as NaN (bf16 and fp32 entry) and must hold none after
+    (k = 3: one index per lookup, k = 4: the pair table)."""
     for M, N, K in ((1, 300, 512), (4, 1000, 3584), (3, 77, 1024)):
-        X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=3, seed=M)
+        X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kb, seed=M)
         d = [t.cuda() for t in (X, ps[0], As[0], cb, rs[0])]
         Y = torch.full_like(d[4], float("nan"))
-        sk.kbit_gemv(d[0], d[1], d[2], d[3], 3, d[4], out=Y)
+        sk.kbit_gemv(d[0], d[1], d[2], d[3], kb, d[4], out=Y)
         A = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-        sk.kbit_gemv_acc_f32(d[0], d[1], d[2], d[3], 3, d[4], out=A)
+        sk.kbit_gemv_acc_f32(d[0], d[1], d[2], d[3], kb, d[4], out=A)
         torch.cuda.synchronize()
         assert not torch.isnan(Y.float()).any() and not torch.isnan(A).any(), (M, N, K)
