@@ -86,3 +86,10 @@ def test_bad_config_shard_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mode", "sweep", "--config-shard", "2",
                         "--num-config-shards", "2"], capture_output=True, text=True, timeout=120)
     assert p.returncode == 2 and "--config-shard" in p.stderr
+
+
+def test_bad_kda_layout_is_refused():
+    p = subprocess.run([sys.executable, "-c", "import sys, types; sys.argv = ['bench.py']; import bench; "
+                        "bench.run_kda(types.SimpleNamespace(ms='1', layouts='ring,bogus', out=None), None)"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert p.returncode != 0 and "--layouts" in p.stderr
