@@ -18,9 +18,9 @@
 //     c, c+8, c+16, c+24 into one word whose bytes are the four indices times 4, i.e. the
 //     LDS byte addresses of their codebook entries; one rotation re-aligns the word; one
 //     bit-field extract per element feeds a ds_read_b32 (the 2^k-entry fp32 table spans at
-//     most 32 banks, so every lookup is conflict-free). For k = 2 and 4 the words instead
+//     most 32 banks, so every lookup is conflict-free). For k = 2, 3 and 4 the words instead
 //     hold two indices per field, and one ds_read_b64 fetches both codebook values from a
-//     table of pairs (block_dot_pair);
+//     table of pairs (block_dot_pair); k = 5 keeps one index per lookup;
 //   * one fp32 FMA per weight and row; the block's sum is scaled once by its decoded absmax;
 //   * per-block partial sums meet in LDS; 16 lanes per output row add them and write
 //     bf16(sum + R) with one rounding (R is loaded by the writing lane at kernel start).
@@ -101,19 +101,23 @@ __device__ __forceinline__ void block_dot(const uint32_t (&P)[KB], uint32_t a, c
     for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
 }
 
-// k = 2 and 4: the same partial sum with two indices per lookup. Word c' (c' in [0, 8) with
-// c' mod 2k < k) of each half of the block collects the elements e, e + k, e + 16, e + 16 + k
-// (e = c' in the low half, c' + 8 in the high half; the words cover all 32 elements): plane i is
-// rotated once per half so that element j's bit lands at j + 3 + i (low) or j - 5 + i (high),
-// and one AND-OR per plane with the mask of positions c' + 3 + i + {0, k, 16, 16 + k} leaves
-// index(e) + index(e + k) << k at bits c' + 3 ... and index(e + 16) + index(e + 16 + k) << k at
-// bits c' + 19 ..., each field 3 + 2k bits long with its low 3 bits clear: one bit-field extract
-// gives the byte address of a float2 (codebook[a], codebook[b]) in a 2^(2k)-entry LDS table.
-// Per 4 weights: k + 2 VALU instructions and two 8-byte lookups (the byte form: k + 5 and four).
+// k = 2, 3 and 4: the same partial sum with two indices per lookup. Each index takes an F-bit
+// field (F = 2 for k = 2, 4 for k = 3 and 4; at k = 3 the top bit is always clear). Word c'
+// (c' in [0, 8) with c' mod 2F < F) of each half of the block collects the elements e, e + F,
+// e + 16, e + 16 + F (e = c' in the low half, c' + 8 in the high half; the words cover all 32
+// elements): plane i is rotated once per half so that element j's bit lands at j + 3 + i (low)
+// or j - 5 + i (high), and one AND-OR per plane with the mask of positions c' + 3 + i + {0, F,
+// 16, 16 + F} leaves index(e) + index(e + F) << F at bits c' + 3 ... and index(e + 16) +
+// index(e + 16 + F) << F at bits c' + 19 ..., each field 3 + 2F bits long with its low 3 bits
+// clear: one bit-field extract gives the byte address of a float2 (codebook[a], codebook[b])
+// in a 2^(2F)-entry LDS table. Per 4 weights: k + 2 VALU instructions and two 8-byte lookups
+// (the byte form: k + 5 and four). k = 5 keeps the byte form: 5-bit fields at distance 5 do not
+// tile a 16-element half.
 template <int KB, int MT>
 __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t a, const float (&x)[MT][32],
                                                const uint32_t (&pm)[7], const char *pairb, float (&out)[MT]) {
-    constexpr int FW = 3 + 2 * KB;                     // field width in bits
+    constexpr int KF = KB == 2 ? 2 : 4;                // field stride: element distance in a pair
+    constexpr int FW = 3 + 2 * KF;                     // field width in bits
     uint32_t Qlo[KB], Qhi[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -127,7 +131,7 @@ __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int cp = 0; cp < 8; ++cp) {
-            if (cp % (2 * KB) >= KB) continue;
+            if (cp % (2 * KF) >= KF) continue;
             const uint32_t(&Q)[KB] = h ? Qhi : Qlo;
             uint32_t w = Q[0] & pm[cp];
 #pragma unroll
@@ -140,9 +144,9 @@ __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 s[m] = fmaf(x[m][e], v0.x, s[m]);
-                s[m] = fmaf(x[m][e + KB], v0.y, s[m]);
+                s[m] = fmaf(x[m][e + KF], v0.y, s[m]);
                 s[m] = fmaf(x[m][e + 16], v1.x, s[m]);
-                s[m] = fmaf(x[m][e + 16 + KB], v1.y, s[m]);
+                s[m] = fmaf(x[m][e + 16 + KF], v1.y, s[m]);
             }
         }
     }
@@ -163,9 +167,11 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
                                                                 const uint16_t *R, void *out, int M, int N, int K,
                                                                 int r, int G) {
     constexpr int L = 1 << KB;
-    constexpr bool PAIR = KB == 2 || KB == 4;   // two indices per lookup (block_dot_pair)
+    constexpr bool PAIR = KB <= 4;               // two indices per lookup (block_dot_pair)
+    constexpr int KF = KB == 2 ? 2 : 4;          // its field stride
+    constexpr int LP = PAIR ? 1 << (2 * KF) : 1; // pair-table entries
     __shared__ float cbs[L];
-    __shared__ float2 pairs[PAIR ? L * L : 1];
+    __shared__ float2 pairs[LP];
     extern __shared__ float part[];        // [r * G][MT][BPR]
 
     const int tid = threadIdx.x;
@@ -215,16 +221,20 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
     asm volatile("" : "+v"(cbv) :: "memory");
     if (lane < L) cbs[lane] = cbv;
     if constexpr (PAIR) {
-        // the pair table, also per wave: entry a + (b << k) = (codebook[a], codebook[b]), read
-        // from this wave's own codebook writes above (a wave's LDS operations run in order)
+        // the pair table, also per wave: entry a + (b << F) = (codebook[a], codebook[b]), read
+        // from this wave's own codebook writes above (a wave's LDS operations run in order);
+        // at k = 3 the entries with a or b >= 8 are never read (clamped here)
 #pragma unroll
-        for (int e0 = 0; e0 < L * L; e0 += 64)
-            if (e0 + lane < L * L) pairs[e0 + lane] = make_float2(cbs[(e0 + lane) & (L - 1)], cbs[(e0 + lane) >> KB]);
+        for (int e0 = 0; e0 < LP; e0 += 64)
+            if (e0 + lane < LP) {
+                const int ea = (e0 + lane) & ((1 << KF) - 1), eb = (e0 + lane) >> KF;
+                pairs[e0 + lane] = make_float2(cbs[min(ea, L - 1)], cbs[min(eb, L - 1)]);
+            }
     }
-    uint32_t pm[7];                              // pair masks: positions s + 3 + {0, k, 16, 16 + k}
+    uint32_t pm[7];                              // pair masks: positions s + 3 + {0, F, 16, 16 + F}
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-        pm[j] = rotl_c((1u | (1u << KB) | (1u << 16) | (1u << (16 + KB))) << 3, j);
+        pm[j] = rotl_c((1u | (1u << KF) | (1u << 16) | (1u << (16 + KF))) << 3, j);
         asm("" : "+v"(pm[j]));
     }
     uint32_t msk[8];

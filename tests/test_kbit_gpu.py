@@ -109,11 +109,12 @@ def test_kbit_k_zero_is_residual(sk):
     assert torch.equal(Y.cpu().view(torch.int16), R.cpu().view(torch.int16))
 
 
-@pytest.mark.parametrize("kb", [3, 4])
+@pytest.mark.parametrize("kb", [3, 4, 5])
 @pytest.mark.parametrize("M,K", [(2, 16384), (1, 14336), (4, 8192)])
 def test_kbit_long_rows(sk, kb, M, K):
     """Long rows: one lane per block up to 512 blocks, a row group of one row per workgroup;
-    k = 3 takes the one-index-per-lookup decode, k = 4 the pair table."""
+    k = 3 and 4 take the pair table (4-bit index fields, the top one clear at k = 3), k = 5 the
+    one-index-per-lookup decode."""
     X, ps, As, rs, cb = synth.make_kbit_inputs(M, 48, K, kbits=kb, seed=K + kb)
     Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, kb, rs[0])
     Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), kb, synth.bits(rs[0]))
@@ -121,10 +122,10 @@ def test_kbit_long_rows(sk, kb, M, K):
     P.check_acc(Ag, Ao, "kbit %d long K=%d" % (kb, K))
 
 
-@pytest.mark.parametrize("kb", [3, 4])
+@pytest.mark.parametrize("kb", [3, 5])
 def test_kbit_poisoned_output_fully_written(sk, kb):
     """Every output is written: Y starts as NaN (bf16 and fp32 entry) and must hold none after
-    (k = 3: one index per lookup, k = 4: the pair table)."""
+    (k = 3: the pair table, k = 5: one index per lookup)."""
     for M, N, K in ((1, 300, 512), (4, 1000, 3584), (3, 77, 1024)):
         X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kb, seed=M)
         d = [t.cuda() for t in (X, ps[0], As[0], cb, rs[0])]
