@@ -20,7 +20,8 @@
 //     bit-field extract per element feeds a ds_read_b32 (the 2^k-entry fp32 table spans at
 //     most 32 banks, so every lookup is conflict-free). For k = 2, 3 and 4 the words instead
 //     hold two indices per field, and one ds_read_b64 fetches both codebook values from a
-//     table of pairs (block_dot_pair); k = 5 keeps one index per lookup;
+//     table of pairs (block_dot_pair); k = 5 pairs the elements 8 apart, whose indices sit
+//     in adjacent bytes of the collected word, in a sparse table (block_dot_pair8);
 //   * one fp32 FMA per weight and row; the block's sum is scaled once by its decoded absmax;
 //   * per-block partial sums meet in LDS; 16 lanes per output row add them and write
 //     bf16(sum + R) with one rounding (R is loaded by the writing lane at kernel start).
@@ -111,8 +112,8 @@ __device__ __forceinline__ void block_dot(const uint32_t (&P)[KB], uint32_t a, c
 // index(e + 16 + F) << F at bits c' + 19 ..., each field 3 + 2F bits long with its low 3 bits
 // clear: one bit-field extract gives the byte address of a float2 (codebook[a], codebook[b])
 // in a 2^(2F)-entry LDS table. Per 4 weights: k + 2 VALU instructions and two 8-byte lookups
-// (the byte form: k + 5 and four). k = 5 keeps the byte form: 5-bit fields at distance 5 do not
-// tile a 16-element half.
+// (the byte form: k + 5 and four). k = 5 takes block_dot_pair8: 5-bit fields at distance 5 do
+// not tile a 16-element half.
 template <int KB, int MT>
 __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t a, const float (&x)[MT][32],
                                                const uint32_t (&pm)[7], const char *pairb, float (&out)[MT]) {
@@ -155,6 +156,45 @@ __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t
     for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
 }
 
+// k = 5: the word of the byte form (byte t of rotr(w, c) holds index(c + 8t) times 8, with
+// planes rotated one place further than there) read as two half-words: the low half-word is
+// 8 * (index(c) + 256 * index(c + 8)) and the high one the same for c + 16 and c + 24, the
+// byte addresses of float2 entries (codebook[a], codebook[b]) at a + 256 b of a sparse LDS
+// table (32 x 32 used entries of 7968). Per 4 weights: 8 VALU instructions (7 at c = 0) and
+// two 8-byte lookups, against 10 and four lookups in the byte form.
+template <int MT>
+__device__ __forceinline__ void block_dot_pair8(const uint32_t (&P)[5], uint32_t a, const float (&x)[MT][32],
+                                                const uint32_t (&m8)[8], const char *pairb, float (&out)[MT]) {
+    uint32_t Q[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) Q[i] = rotr(P[i], 29 - i);   // element j, plane i -> bit j + 3 + i
+    float s[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        // plane i of elements c + 8t sits at bits 8t + 3 + i + c (mod 32): mask m8[(c + i) % 8]
+        uint32_t w = Q[0] & m8[c];
+#pragma unroll
+        for (int i = 1; i < 5; ++i) w = and_or(Q[i], m8[(c + i) & 7], w);
+        if (c) w = rotr(w, c);
+        asm("" : "+v"(w));                                       // one instruction per half-word
+        const uint32_t f0 = w & 0xFFFFu, f1 = w >> 16;
+        const float2 v0 = *reinterpret_cast<const float2 *>(pairb + f0);
+        const float2 v1 = *reinterpret_cast<const float2 *>(pairb + f1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            s[m] = fmaf(x[m][c], v0.x, s[m]);
+            s[m] = fmaf(x[m][c + 8], v0.y, s[m]);
+            s[m] = fmaf(x[m][c + 16], v1.x, s[m]);
+            s[m] = fmaf(x[m][c + 24], v1.y, s[m]);
+        }
+    }
+    const float scale = e4m4_decode(a);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) out[m] = s[m] * scale;
+}
+
 // One launch: grid.x = ceil(N / (r * G)), grid.y = ceil(M / MT); blockDim.x = T (a multiple of
 // 64 with r * BPR <= T and r * G <= T / 16); K >= 32. Lane t < r * BPR owns row offset t / BPR and
 // block t % BPR; the other lanes compute a clamped copy that is not stored, and help with the
@@ -168,8 +208,9 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
                                                                 int r, int G) {
     constexpr int L = 1 << KB;
     constexpr bool PAIR = KB <= 4;               // two indices per lookup (block_dot_pair)
-    constexpr int KF = KB == 2 ? 2 : 4;          // its field stride
-    constexpr int LP = PAIR ? 1 << (2 * KF) : 1; // pair-table entries
+    constexpr bool PAIR8 = KB == 5;              // the same with pairs 8 apart (block_dot_pair8)
+    constexpr int KF = KB == 2 ? 2 : 4;          // block_dot_pair's field stride
+    constexpr int LP = PAIR ? 1 << (2 * KF) : PAIR8 ? 31 + 256 * 31 + 1 : 1;  // pair-table entries
     __shared__ float cbs[L];
     __shared__ float2 pairs[LP];
     extern __shared__ float part[];        // [r * G][MT][BPR]
@@ -184,10 +225,16 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
     const int blk = active ? tid - roff * BPR : 0;
 
     // every load is unconditional (clamped addresses) and issued before the first wait, in
-    // the order the data is needed (the memory counter is waited on in issue order): X of this
-    // lane's block, the writer lanes' residuals, then the plane words and scale bytes of all
-    // kMaxRowGroups row groups (groups past G repeat group G - 1 and are not used). The
-    // codebook load is issued first.
+    // about the order the data is needed (the memory counter is waited on in issue order): X
+    // of this lane's block, the writer lanes' residuals, then the plane words and scale bytes
+    // of all kMaxRowGroups row groups (groups past G repeat group G - 1 and are not used). The
+    // codebook load is issued first. Where the words and the scale bytes go is the compiler's
+    // choice (the empty asm statements do not bind loads of memory the kernel never writes);
+    // the two source forms below lead it to different schedules, chosen per k by measurement
+    // at K = 3584 (0.1 - 0.5 us apart). The schedule to avoid: the first group's scale byte
+    // issued behind every word and widened before the pair-table writes, which makes the
+    // first wait one for all loads (k = 5 took it when its words and bytes were loaded in one
+    // loop).
     const int lane = tid & 63;
     float cbv = codebook[lane & (L - 1)];
     asm volatile("" ::: "memory");             // the codebook load stays first
@@ -206,13 +253,29 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
 
     uint32_t P[kMaxRowGroups][KB];
     uint32_t A[kMaxRowGroups];
+    if constexpr (KB == 3 || KB == 5) {
+        size_t bi[kMaxRowGroups];
 #pragma unroll
-    for (int g = 0; g < kMaxRowGroups; ++g) {
-        const int n = min(n0 + min(g, G - 1) * r + roff, N - 1);
-        const size_t b = (size_t)n * BPR + blk;
+        for (int g = 0; g < kMaxRowGroups; ++g) {
+            const int n = min(n0 + min(g, G - 1) * r + roff, N - 1);
+            bi[g] = (size_t)n * BPR + blk;
+            A[g] = absmax[bi[g]];
+        }
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < KB; ++i) P[g][i] = __builtin_nontemporal_load(planes + b * KB + i);
-        A[g] = absmax[b];
+        for (int g = 0; g < kMaxRowGroups; ++g)
+#pragma unroll
+            for (int i = 0; i < KB; ++i) P[g][i] = __builtin_nontemporal_load(planes + bi[g] * KB + i);
+    } else {
+#pragma unroll
+        for (int g = 0; g < kMaxRowGroups; ++g) {
+            const int n = min(n0 + min(g, G - 1) * r + roff, N - 1);
+            const size_t b = (size_t)n * BPR + blk;
+#pragma unroll
+            for (int i = 0; i < KB; ++i) P[g][i] = __builtin_nontemporal_load(planes + b * KB + i);
+            A[g] = absmax[b];
+            asm volatile("" ::: "memory");
+        }
     }
 
     // every wave writes the whole codebook itself (all waves write identical values), so
@@ -231,17 +294,25 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
                 pairs[e0 + lane] = make_float2(cbs[min(ea, L - 1)], cbs[min(eb, L - 1)]);
             }
     }
+    if constexpr (PAIR8) {
+        // the 32 x 32 used entries a + 256 b, per wave as above: lane l writes a = l % 32 (its
+        // own codebook value) for b = 2 i + l / 32, i = 0..15
+        float2 *prow = pairs + (lane & 31) + 256 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) prow[512 * i] = make_float2(cbv, cbs[2 * i + (lane >> 5)]);
+    }
     uint32_t pm[7];                              // pair masks: positions s + 3 + {0, F, 16, 16 + F}
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
         pm[j] = rotl_c((1u | (1u << KF) | (1u << 16) | (1u << (16 + KF))) << 3, j);
         asm("" : "+v"(pm[j]));
     }
-    uint32_t msk[8];
+    uint32_t msk[8], m8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         msk[j] = rotl_c(0x04040404u, j);
-        asm("" : "+v"(msk[j]));                  // keep in VGPRs: a VOP3 AND-OR takes no literal
+        m8[j] = rotl_c(0x08080808u, j);
+        asm("" : "+v"(msk[j]), "+v"(m8[j]));     // keep in VGPRs: a VOP3 AND-OR takes no literal
     }
     // X to fp32: pinning xv here keeps its wait (and the conversion) from being scheduled
     // between the loads above, where it would hold back their issue
@@ -273,6 +344,9 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
             if constexpr (PAIR) {
                 block_dot_pair<KB, MT>(P[g], A[g], x, pm, pairb, o0);
                 block_dot_pair<KB, MT>(P[g + 1], A[g + 1], x, pm, pairb, o1);
+            } else if constexpr (PAIR8) {
+                block_dot_pair8<MT>(P[g], A[g], x, m8, pairb, o0);
+                block_dot_pair8<MT>(P[g + 1], A[g + 1], x, m8, pairb, o1);
             } else {
                 block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
                 block_dot<KB, MT>(P[g + 1], A[g + 1], x, msk, cbb, o1);
@@ -289,6 +363,7 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
         } else if (g < G) {
             float o0[MT];
             if constexpr (PAIR) block_dot_pair<KB, MT>(P[g], A[g], x, pm, pairb, o0);
+            else if constexpr (PAIR8) block_dot_pair8<MT>(P[g], A[g], x, m8, pairb, o0);
             else block_dot<KB, MT>(P[g], A[g], x, msk, cbb, o0);
             if (active) {
                 float *p0 = part + (size_t)(g * r + roff) * MT * BPR + blk;
