@@ -29,7 +29,7 @@ Other modes write JSONL rows (one per configuration or M) to --out:
                   H = HV = 8, K = V = 128, T = 4, B in --ms (default 1,4,16,64), snapshot and ring
                   mode; states and outputs rotate over enough copies to exceed 320 MB
   --mode kbit     the k-bit quantized decode GEMV (bitsandbytes page "compare/main...QLORA-2.diff"),
-                  N = 7168, K = 3584, k in --kbits, M in --ms (default 1,2,4); the planes and
+                  N = 7168, K = 3584, k in --kbits, M in --ms (default 1,2,4,16); the planes and
                   scale bytes rotate over enough copies to exceed 308 MB
 """
 from __future__ import annotations
@@ -723,7 +723,7 @@ def run_kbit(args, sk):
     import torch
 
     import oracle
-    Ms = [int(x) for x in args.ms.split(",")] if args.ms else [1, 2, 4]
+    Ms = [int(x) for x in args.ms.split(",")] if args.ms else [1, 2, 4, 16]
     kbs = [int(x) for x in args.kbits.split(",")]
     out = open(args.out, "a") if args.out else None
     for kb in kbs:

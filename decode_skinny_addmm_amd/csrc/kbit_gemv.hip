@@ -394,6 +394,225 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Matrix-core form for 5 <= M (k = 2 and 4; K a multiple of 128, at most 3584; the plane words
+// of a block read as one 8- or 16-byte vector, the scale bytes of four blocks as one dword): the
+// products go to v_mfma_f32_16x16x32_bf16 with X as the A operand (16 rows of X) and the decoded
+// weights as the B operand (16 W rows), so one MFMA covers one 32-element block of 16 W rows
+// for up to 16 rows of X. A W row's block is split over four lanes (lane l: W row l % 16, part
+// g = l / 16), each decoding two of the pair words of block_dot_pair (planes rotated one bit
+// further, so a field is the entry index times 16): 8 elements per lane, in the order e, e + F,
+// e + 16, e + 16 + F for its two word positions; X's fragments take the same order. A pair-table
+// entry holds the two codebook values as three bf16 pairs (hi, mid, lo: each fp32 value is
+// exactly the sum of its three bf16 parts, so the three MFMAs reproduce the fp32 products; two
+// parts, 2^-18 relative, miss the parity floor of outputs near zero); the block's
+// D = X . (hi + mid + lo) is then scaled by the lane's W-row absmax (each D lane holds one W row)
+// and added to the accumulator. The time barely depends on M (up to 16): about 60 VALU
+// instructions per block and lane (the decode's rotations now serve 8 elements instead of 32,
+// and 12 moves assemble the B fragments from the 16-byte entries) and conflicting 16-byte LDS
+// lookups, which is why M <= 4 stays with the VALU form.
+constexpr int kMfmaWaves = 7;          // K slices of 16 blocks (512 elements) per workgroup
+constexpr int kMfmaBlocks = 16;        // blocks per wave
+constexpr int kMfmaTiles = 2;          // 16-row W tiles per workgroup
+constexpr int kXPitchB = 1040;         // bytes per staged X row (512 bf16 + 16)
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4 a, u32x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// fp32 -> three bf16 parts whose sum is the value exactly (each part truncated from what the
+// previous ones leave: 8 + 8 + 8 significant bits)
+__device__ __forceinline__ void split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+    const uint32_t b0 = __float_as_uint(v) & 0xFFFF0000u;
+    const float r1 = v - __uint_as_float(b0);
+    const uint32_t b1 = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(b1);
+    hi = b0 >> 16;
+    mid = b1 >> 16;
+    lo = __float_as_uint(r2) >> 16;
+}
+
+template <int KB, bool ACC>
+__global__ __launch_bounds__(kMfmaWaves * 64) void kbit_mfma_kernel(const uint16_t *__restrict__ X,
+                                                                    const uint32_t *__restrict__ planes,
+                                                                    const uint8_t *__restrict__ absmax,
+                                                                    const float *__restrict__ codebook,
+                                                                    const uint16_t *R, void *out, int M, int N,
+                                                                    int K) {
+    static_assert(KB == 2 || KB == 4, "plane words read as one 8- or 16-byte vector");
+    constexpr int L = 1 << KB;
+    constexpr int F = KB == 2 ? 2 : 4;           // pair distance (field stride)
+    constexpr int FW = 4 + 2 * F;                // field width: entry index times 16
+    constexpr int LP = 1 << (2 * F);             // pair-table entries
+    constexpr int NT = kMfmaWaves * 64;
+    constexpr int ROWS = 16 * kMfmaTiles;
+    constexpr int OUTS = ROWS * 16;
+    constexpr int PER = (OUTS + NT - 1) / NT;
+    __shared__ float cbs[L];
+    __shared__ u32x4 pairs[LP];
+    __shared__ __attribute__((aligned(16))) uint8_t xst[kMfmaWaves][16 * kXPitchB];
+    __shared__ f32x4_t red[kMfmaTiles][kMfmaWaves][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int BPR = K >> 5;
+    const int NV = K >> 3;                       // 16-byte vectors of an X row
+    const int n0 = blockIdx.x * ROWS;
+    const int m0 = blockIdx.y * 16;
+    const int b0 = w * kMfmaBlocks;              // this wave's first block
+    const int nb = max(0, min(kMfmaBlocks, BPR - b0));
+    const int rn = lane & 15, g = lane >> 4, h = g >> 1;
+
+    // loads, in the order they are used, all before the first wait: the codebook, this wave's X
+    // slice (16 rows x 512 elements, 1 KB per instruction), the residuals of the outputs this
+    // thread writes, then per tile the scale dwords (16 blocks of the lane's W row) and the plane
+    // words of the lane's W row for each of the wave's blocks (addresses clamped; blocks past the
+    // wave's nb are loaded but never used)
+    float cbv = codebook[lane & (L - 1)];
+    asm volatile("" ::: "memory");
+    u32x4 xr[16];
+    {
+        const int v = min(4 * b0 + lane, NV - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            xr[r] = *reinterpret_cast<const u32x4 *>(X + (size_t)min(m0 + r, M - 1) * K + 8 * v);
+    }
+    uint16_t rbits[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int e = min(tid + p * NT, OUTS - 1);
+        rbits[p] = R[(size_t)min(m0 + e / ROWS, M - 1) * N + min(n0 + e % ROWS, N - 1)];
+    }
+    uint32_t sc[kMfmaTiles][4];
+    uint32_t P[kMfmaTiles][kMfmaBlocks][KB];
+#pragma unroll
+    for (int t = 0; t < kMfmaTiles; ++t) {
+        const size_t row = (size_t)min(n0 + 16 * t + rn, N - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            sc[t][q] = *reinterpret_cast<const uint32_t *>(absmax + row * BPR + min(b0 + 4 * q, BPR - 4));
+#pragma unroll
+        for (int j = 0; j < kMfmaBlocks; ++j) {
+            const uint32_t *pw = planes + (row * BPR + min(b0 + j, BPR - 1)) * KB;
+            if constexpr (KB == 4) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(pw);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) P[t][j][i] = v[i];
+            } else {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(pw);
+                P[t][j][0] = v[0];
+                P[t][j][1] = v[1];
+            }
+        }
+    }
+
+    // the codebook and the pair table of three-part entries, per wave (identical writes in every
+    // wave, read back only by the writing wave: no workgroup barrier); entry a + (b << F)
+    asm volatile("" : "+v"(cbv) :: "memory");
+    if (lane < L) cbs[lane] = cbv;
+#pragma unroll
+    for (int e0 = 0; e0 < LP; e0 += 64)
+        if (e0 + lane < LP) {
+            const int ea = (e0 + lane) & ((1 << F) - 1), eb = (e0 + lane) >> F;
+            uint32_t ha, ma, la, hb, mb, lb;
+            split3(cbs[min(ea, L - 1)], ha, ma, la);
+            split3(cbs[min(eb, L - 1)], hb, mb, lb);
+            pairs[e0 + lane] = u32x4{ha | (hb << 16), ma | (mb << 16), la | (lb << 16), 0u};
+        }
+
+    // X fragments through this wave's LDS slice: lane (row rn, part g) takes, of block j, the
+    // pairs (e, e + F) and (e + 16, e + 16 + F) for its two word positions e = cp + 8h, i.e. from
+    // the 16-byte chunks 4j + h and 4j + 2 + h the dwords p and q (F = 4: p = g % 2, q = p + 2;
+    // F = 2: p = 2 (g % 2), q = p + 1), low halves then high halves
+    uint8_t *xs = xst[w];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        asm volatile("" : "+v"(xr[r]));
+        *reinterpret_cast<u32x4 *>(xs + r * kXPitchB + 16 * lane) = xr[r];
+    }
+    const int pp = F == 4 ? (g & 1) : 2 * (g & 1);
+    const int qq = F == 4 ? pp + 2 : pp + 1;
+    u32x4 xf[kMfmaBlocks];
+#pragma unroll
+    for (int j = 0; j < kMfmaBlocks; ++j) {
+        const uint32_t *ca = reinterpret_cast<const uint32_t *>(xs + rn * kXPitchB + 16 * (4 * j + h));
+        const uint32_t *cb2 = reinterpret_cast<const uint32_t *>(xs + rn * kXPitchB + 16 * (4 * j + 2 + h));
+        const uint32_t ap = ca[pp], aq = ca[qq], bp = cb2[pp], bq = cb2[qq];
+        xf[j] = u32x4{(ap & 0xFFFFu) | (aq << 16), (bp & 0xFFFFu) | (bq << 16), (ap >> 16) | (aq & 0xFFFF0000u),
+                      (bp >> 16) | (bq & 0xFFFF0000u)};
+        if (j >= nb) xf[j] = u32x4{0u, 0u, 0u, 0u};  // past the wave's blocks: products exactly 0
+    }
+
+    // per lane: its two word positions and their masks (plane i of element j at bit j + 4 + i,
+    // 8 lower for the high half)
+    const int cpa = F == 4 ? 2 * (g & 1) : 4 * (g & 1);
+    const int rot = h ? 4 : 28;
+    uint32_t mk[2][KB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const uint32_t base = (1u | (1u << F) | (1u << 16) | (1u << (16 + F))) << 4;
+            mk[u][i] = rotr(base, (32 - (cpa + u + i)) & 31);   // base rotated left by cp + i
+        }
+    const char *pairb = reinterpret_cast<const char *>(pairs);
+
+    f32x4_t acc[kMfmaTiles];
+#pragma unroll
+    for (int t = 0; t < kMfmaTiles; ++t) {
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMfmaBlocks; ++j) {   // blocks past nb add 0 (zero X fragment)
+            uint32_t Q[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) Q[i] = rotr(P[t][j][i], rot - i);
+            u32x4 bh, bm, bl;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t wd = Q[0] & mk[u][0];
+#pragma unroll
+                for (int i = 1; i < KB; ++i) wd = and_or(Q[i], mk[u][i], wd);
+                const int cp = cpa + u;
+                const u32x4 e0 = *reinterpret_cast<const u32x4 *>(pairb + __builtin_amdgcn_ubfe(wd, cp, FW));
+                const u32x4 e1 = *reinterpret_cast<const u32x4 *>(pairb + __builtin_amdgcn_ubfe(wd, cp + 16, FW));
+                bh[2 * u] = e0[0]; bm[2 * u] = e0[1]; bl[2 * u] = e0[2];
+                bh[2 * u + 1] = e1[0]; bm[2 * u + 1] = e1[1]; bl[2 * u + 1] = e1[2];
+            }
+            f32x4_t d = mfma_bf16(xf[j], bh, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            d = mfma_bf16(xf[j], bm, d);
+            d = mfma_bf16(xf[j], bl, d);
+            const float sv = e4m4_decode(__builtin_amdgcn_ubfe(sc[t][j >> 2], 8 * (j & 3), 8));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(d[i], sv, acc[t][i]);
+        }
+        // acc[t][i] = partial Y[m0 + 4g + i][n0 + 16t + rn] over this wave's blocks
+        red[t][w][lane] = acc[t];
+    }
+    __syncthreads();
+
+    const float *redf = reinterpret_cast<const float *>(&red[0][0][0]);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int e = tid + p * NT;
+        if (e >= OUTS) break;
+        const int nl = e % ROWS, mc = e / ROWS;
+        const int m = m0 + mc, n = n0 + nl;
+        if (m >= M || n >= N) continue;
+        const int t = nl >> 4, j = nl & 15;
+        const int idx = (16 * (mc >> 2) + j) * 4 + (mc & 3);
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kMfmaWaves; ++q) v += redf[(t * kMfmaWaves + q) * 64 * 4 + idx];
+        store_output<ACC>(out, Epilogue{N, N, 0u}, m, n, v, bf16_bits_to_f32(rbits[p]));
+    }
+}
+
 struct KbitShape {
     int r, T, G;
     size_t shmem;
@@ -465,6 +684,17 @@ hipError_t launch_kbit_mt(const KbitArgs &a) {
     return launch_kbit<KB, 4>(a);
 }
 
+// The matrix-core form takes k = 2 and 4 from M = 5 (where the VALU form needs a second 4-row
+// pass; at K = 3584: M = 5 .. 8 15.9 against 17.2 - 17.5 us at k = 4, M = 16 16.2 against 33.2)
+// when K fits its 7 x 16 blocks in whole dwords of scale bytes and the plane and scale pointers
+// allow its vector loads; at M <= 4 the VALU form is faster (k = 4, M = 4: 9.4 against 15.9).
+constexpr int64_t kKbitMfmaMinM = 5;
+bool kbit_mfma_eligible(const KbitArgs &a) {
+    const uintptr_t pl = reinterpret_cast<uintptr_t>(a.planes), am = reinterpret_cast<uintptr_t>(a.absmax);
+    return (a.kbits == 2 || a.kbits == 4) && a.M >= kKbitMfmaMinM && a.K % 128 == 0 &&
+           a.K <= 32 * kMfmaWaves * kMfmaBlocks && pl % (4 * a.kbits) == 0 && am % 4 == 0;
+}
+
 }  // namespace
 
 int64_t kbit_max_k() {
@@ -473,6 +703,22 @@ int64_t kbit_max_k() {
 }
 
 hipError_t launch_kbit_gemv(const KbitArgs &a) {
+    if (kbit_mfma_eligible(a)) {
+        const dim3 grid((unsigned)((a.N + 16 * kMfmaTiles - 1) / (16 * kMfmaTiles)), (unsigned)((a.M + 15) / 16));
+        const dim3 block(kMfmaWaves * 64);
+#define KBIT_MFMA(KB, ACC)                                                                                      \
+    hipLaunchKernelGGL((kbit_mfma_kernel<KB, ACC>), grid, block, 0, a.stream, a.X, a.planes, a.absmax, a.codebook, \
+                       a.R, a.out, (int)a.M, (int)a.N, (int)a.K)
+        if (a.kbits == 4) {
+            if (a.acc_out) KBIT_MFMA(4, true);
+            else KBIT_MFMA(4, false);
+        } else {
+            if (a.acc_out) KBIT_MFMA(2, true);
+            else KBIT_MFMA(2, false);
+        }
+#undef KBIT_MFMA
+        return hipGetLastError();
+    }
     switch (a.kbits) {
         case 2: return launch_kbit_mt<2>(a);
         case 3: return launch_kbit_mt<3>(a);

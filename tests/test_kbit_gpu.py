@@ -45,9 +45,25 @@ def test_kbit_matches_oracle(sk, kb, M, N, K):
     assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
 
 
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("kb", [2, 4])
+@pytest.mark.parametrize("M,N,K", [(5, 130, 512), (8, 64, 3584), (16, 300, 1024), (17, 40, 128), (40, 33, 384),
+                                   (9, 1000, 2048)])
+def test_kbit_matrix_core_form(sk, kb, M, N, K):
+    """M >= 5 with k = 2 and 4 and K a multiple of 128 (at most 3584) run on the matrix cores:
+    one and several 16-row passes over X, ragged N, waves whose K slice is partly or wholly past K."""
+    X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kb, seed=M * 100 + kb + 7)
+    print("kbit mfma", kb, (M, N, K), flush=True)
+    Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, kb, rs[0])
+    Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), kb, synth.bits(rs[0]))
+    P.check_y(Yg, Yo, Ao, "kbit mfma %d %s" % (kb, (M, N, K)))
+    P.check_acc(Ag, Ao, "kbit mfma %d %s" % (kb, (M, N, K)))
+    assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
 def test_kbit_full_size(sk, M):
-    """The decode shape, N = 7168, K = 3584, k = 4, against the whole oracle."""
+    """The decode shape, N = 7168, K = 3584, k = 4, against the whole oracle (M = 16: the matrix-
+    core form)."""
     X, ps, As, rs, cb = synth.make_kbit_inputs(M, 7168, 3584, kbits=4)
     Yg, Ag = run_gpu(sk, X, ps[0], As[0], cb, 4, rs[0])
     Yo, Ao = oracle.kbit_gemv_bf16(synth.bits(X), _u32(ps[0]), As[0].numpy(), cb.numpy(), 4, synth.bits(rs[0]))
@@ -110,7 +126,7 @@ def test_kbit_k_zero_is_residual(sk):
 
 
 @pytest.mark.parametrize("kb", [3, 4, 5])
-@pytest.mark.parametrize("M,K", [(2, 16384), (1, 14336), (4, 8192)])
+@pytest.mark.parametrize("M,K", [(2, 16384), (1, 14336), (4, 8192), (8, 4096)])
 def test_kbit_long_rows(sk, kb, M, K):
     """Long rows: one lane per block up to 512 blocks, a row group of one row per workgroup;
     k = 3 and 4 take the pair table (4-bit index fields, the top one clear at k = 3), k = 5 the
@@ -122,11 +138,11 @@ def test_kbit_long_rows(sk, kb, M, K):
     P.check_acc(Ag, Ao, "kbit %d long K=%d" % (kb, K))
 
 
-@pytest.mark.parametrize("kb", [3, 5])
+@pytest.mark.parametrize("kb", [3, 4, 5])
 def test_kbit_poisoned_output_fully_written(sk, kb):
     """Every output is written: Y starts as NaN (bf16 and fp32 entry) and must hold none after
-    (k = 3: the pair table, k = 5: one index per lookup)."""
-    for M, N, K in ((1, 300, 512), (4, 1000, 3584), (3, 77, 1024)):
+    (k = 3: the pair table, k = 5: pairs 8 apart, k = 4 at M >= 5: the matrix-core form)."""
+    for M, N, K in ((1, 300, 512), (4, 1000, 3584), (3, 77, 1024), (21, 70, 1024)):
         X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kb, seed=M)
         d = [t.cuda() for t in (X, ps[0], As[0], cb, rs[0])]
         Y = torch.full_like(d[4], float("nan"))
