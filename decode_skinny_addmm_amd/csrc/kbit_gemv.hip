@@ -395,8 +395,8 @@ __global__ __launch_bounds__(kMaxThreads) void kbit_gemv_kernel(const uint16_t *
 }
 
 // ---------------------------------------------------------------------------------------------
-// Matrix-core form for 5 <= M (k = 2 and 4; K a multiple of 128, at most 3584; the plane words
-// of a block read as one 8- or 16-byte vector, the scale bytes of four blocks as one dword): the
+// Matrix-core form for 5 <= M (k = 2, 3 and 4; K a multiple of 128, at most 3584; the plane
+// words of a block read as one 8-, 12- or 16-byte vector, the scale bytes of four blocks as one dword): the
 // products go to v_mfma_f32_16x16x32_bf16 with X as the A operand (16 rows of X) and the decoded
 // weights as the B operand (16 W rows), so one MFMA covers one 32-element block of 16 W rows
 // for up to 16 rows of X. A W row's block is split over four lanes (lane l: W row l % 16, part
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void kbit_mfma_kernel(const uint16
                                                                     const float *__restrict__ codebook,
                                                                     const uint16_t *R, void *out, int M, int N,
                                                                     int K) {
-    static_assert(KB == 2 || KB == 4, "plane words read as one 8- or 16-byte vector");
+    static_assert(KB >= 2 && KB <= 4, "plane words read as one 8-, 12- or 16-byte vector");
     constexpr int L = 1 << KB;
     constexpr int F = KB == 2 ? 2 : 4;           // pair distance (field stride)
     constexpr int FW = 4 + 2 * F;                // field width: entry index times 16
@@ -504,6 +504,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void kbit_mfma_kernel(const uint16
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(pw);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) P[t][j][i] = v[i];
+            } else if constexpr (KB == 3) {
+                const uint3 v = *reinterpret_cast<const uint3 *>(pw);   // one 12-byte load
+                P[t][j][0] = v.x;
+                P[t][j][1] = v.y;
+                P[t][j][2] = v.z;
             } else {
                 const u32x2 v = *reinterpret_cast<const u32x2 *>(pw);
                 P[t][j][0] = v[0];
@@ -684,15 +689,16 @@ hipError_t launch_kbit_mt(const KbitArgs &a) {
     return launch_kbit<KB, 4>(a);
 }
 
-// The matrix-core form takes k = 2 and 4 from M = 5 (where the VALU form needs a second 4-row
+// The matrix-core form takes k = 2, 3 and 4 from M = 5 (where the VALU form needs a second 4-row
 // pass; at K = 3584: M = 5 .. 8 15.9 against 17.2 - 17.5 us at k = 4, M = 16 16.2 against 33.2)
 // when K fits its 7 x 16 blocks in whole dwords of scale bytes and the plane and scale pointers
 // allow its vector loads; at M <= 4 the VALU form is faster (k = 4, M = 4: 9.4 against 15.9).
 constexpr int64_t kKbitMfmaMinM = 5;
 bool kbit_mfma_eligible(const KbitArgs &a) {
     const uintptr_t pl = reinterpret_cast<uintptr_t>(a.planes), am = reinterpret_cast<uintptr_t>(a.absmax);
-    return (a.kbits == 2 || a.kbits == 4) && a.M >= kKbitMfmaMinM && a.K % 128 == 0 &&
-           a.K <= 32 * kMfmaWaves * kMfmaBlocks && pl % (4 * a.kbits) == 0 && am % 4 == 0;
+    const uintptr_t pal = a.kbits == 3 ? 4 : 4 * a.kbits;   // 12-byte words: dword alignment
+    return a.kbits <= 4 && a.M >= kKbitMfmaMinM && a.K % 128 == 0 && a.K <= 32 * kMfmaWaves * kMfmaBlocks &&
+           pl % pal == 0 && am % 4 == 0;
 }
 
 }  // namespace
@@ -712,6 +718,9 @@ hipError_t launch_kbit_gemv(const KbitArgs &a) {
         if (a.kbits == 4) {
             if (a.acc_out) KBIT_MFMA(4, true);
             else KBIT_MFMA(4, false);
+        } else if (a.kbits == 3) {
+            if (a.acc_out) KBIT_MFMA(3, true);
+            else KBIT_MFMA(3, false);
         } else {
             if (a.acc_out) KBIT_MFMA(2, true);
             else KBIT_MFMA(2, false);

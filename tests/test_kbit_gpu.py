@@ -45,11 +45,11 @@ def test_kbit_matches_oracle(sk, kb, M, N, K):
     assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1))
 
 
-@pytest.mark.parametrize("kb", [2, 4])
+@pytest.mark.parametrize("kb", [2, 3, 4])
 @pytest.mark.parametrize("M,N,K", [(5, 130, 512), (8, 64, 3584), (16, 300, 1024), (17, 40, 128), (40, 33, 384),
                                    (9, 1000, 2048)])
 def test_kbit_matrix_core_form(sk, kb, M, N, K):
-    """M >= 5 with k = 2 and 4 and K a multiple of 128 (at most 3584) run on the matrix cores:
+    """M >= 5 with k = 2, 3 and 4 and K a multiple of 128 (at most 3584) run on the matrix cores:
     one and several 16-row passes over X, ragged N, waves whose K slice is partly or wholly past K."""
     X, ps, As, rs, cb = synth.make_kbit_inputs(M, N, K, kbits=kb, seed=M * 100 + kb + 7)
     print("kbit mfma", kb, (M, N, K), flush=True)
