@@ -212,9 +212,12 @@ SKINNY_API skinny_status skinny_addmm_bf16_shard_acc_f32(const void *X, const vo
  *   codebook float [2^kbits] (e.g. the normal-float levels); 4-byte aligned
  *   R, Y     bf16 [M, N] row-major (Y may be exactly R)
  * kbits is 2..5 (else SKINNY_EINVAL); K must be a multiple of 32 and at most 16384 (one lane
- * per 32-element block of a row, 512 lanes per workgroup), else SKINNY_ENOTSUP. Sums are fp32, one RNE rounding. M of any size runs in passes
- * of up to 4 rows (the kernel is meant for decode, M <= 4). Same conventions as above
- * otherwise (device pointers, asynchronous, no allocation).
+ * per 32-element block of a row, 512 lanes per workgroup), else SKINNY_ENOTSUP. Sums are fp32,
+ * one RNE rounding. M of any size runs in passes: of up to 4 rows on the VALU (the decode
+ * form), or, for M >= 5 with kbits 2..4, K a multiple of 128 up to 3584, planes aligned to
+ * 4 * kbits bytes (4 at kbits 3) and absmax to 4, of up to 16 rows on the matrix cores, with
+ * each codebook value split into three bf16 parts whose sum is that fp32 value exactly. Same
+ * conventions as above otherwise (device pointers, asynchronous, no allocation).
  */
 SKINNY_API skinny_status skinny_kbit_gemv_bf16(const void *X, const uint32_t *planes, const uint8_t *absmax,
                                                const float *codebook, int32_t kbits, const void *R, void *Y,
