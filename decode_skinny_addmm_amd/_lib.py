@@ -17,6 +17,7 @@ PATH_GEMM = 3
 PATH_SIMT = 4
 PATH_GEMM_DMA = 5
 PATH_GEMM_RING = 6
+PATH_GEMM_WS = 7
 FLAG_ROUND_PRODUCT = 1  # shard epilogue: round the product sum to bf16, add R, round again
 FLAG_NO_NEG_ZERO = 2    # shard epilogue: write +0 for a -0 result
 CONFIG_FIELDS = ("path", "block_size", "outputs_per_block", "k_unroll", "vector_width", "m_tile", "k_split",

@@ -170,7 +170,8 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
         c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0 ||
-        (c.path == SKINNY_PATH_GEMM_RING ? (c.k_stage != 64 && c.k_stage != 128) : c.k_stage != 0))
+        ((c.path == SKINNY_PATH_GEMM_RING || c.path == SKINNY_PATH_GEMM_WS) ? (c.k_stage != 64 && c.k_stage != 128)
+                                                                           : c.k_stage != 0))
         return SKINNY_EINVAL;
     const KernelEntry *e = find_entry(c, M);
     if (!e) return SKINNY_ENOTSUP;

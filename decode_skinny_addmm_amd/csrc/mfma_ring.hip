@@ -24,6 +24,7 @@
 //     adds the K-step groups in wave order and R in fp32, rounds once to bf16 and writes Y
 //     row-contiguously;
 //   * blocks are ordered so the m-tiles sharing one W tile run consecutively on one XCD.
+// A second kernel below runs the same ring with the waves split into loaders and compute waves.
 // K must be a multiple of KC.
 #include "common.hpp"
 
@@ -248,6 +249,212 @@ hipError_t launch_ring(const LaunchArgs &a) {
     return hipGetLastError();
 }
 
+// Wave-specialised form (path SKINNY_PATH_GEMM_WS): the same ring, blocks, swizzle and
+// epilogue, but each wave of a workgroup has one role. NL loader waves only issue the
+// direct-to-LDS loads: each waits for its own loads of a stage, meets the stage barrier and
+// refills the slot that barrier freed. NC = WK x WN x WM compute waves only read fragments and
+// run the matrix instructions. In the form above every wave issues its share of the next stage
+// and then stalls until the memory pipeline takes it (a third of a stage's time at M = 256),
+// with its matrix work queued behind the stall; here the stalls fall on waves that have nothing
+// else to do, while the compute waves on the same SIMDs keep the matrix cores busy.
+// SPLIT: the first NL / 2 loaders take a stage's W rows and the others its X rows, so no
+// wave's in-order load completions mix HBM and L2 latencies; otherwise loader lw takes the
+// stage's load blocks NL*i + lw.
+//
+// One loader's part of the ring: PW load blocks (1 KB) per stage, block q = first + step*i
+// holding rows RPL*q ... of the stage (its W rows first, then its X rows); the first NWI of
+// them are W rows and carry the non-temporal policy. Lane l fills position l of a block, as in
+// the kernel above.
+template <int BN, int BM, int KC, int NS, int PW, int NWI>
+__device__ __forceinline__ void ring_loader(const uint16_t *X, const uint16_t *W, int M, int N, int K, int n0,
+                                            int m0, int lane, int first, int step, uint8_t *lds, int S) {
+    constexpr int RB = KC * 2, CPR = RB / 16, RPL = 1024 / RB;
+    constexpr int STAGE_BYTES = (BN + BM) * RB;
+    const uint16_t *src[PW];
+    int dst[PW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+        const int q = first + step * i;
+        const int sr = RPL * q + lane / CPR;
+        const int c = (lane % CPR) ^ swizzle<RB>(sr);
+        const uint16_t *row = sr < BN ? W + (size_t)min(n0 + sr, N - 1) * K
+                                      : X + (size_t)min(m0 + sr - BN, M - 1) * K;
+        src[i] = row + 8 * c;
+        dst[i] = q * 1024;
+    }
+    auto issue = [&](int s) {                        // stage s -> ring slot s % NS
+        lds_u8 *st = (lds_u8 *)(lds + (s % NS) * STAGE_BYTES);
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+            if (i < NWI)
+                __builtin_amdgcn_global_load_lds((const void *)(src[i] + (size_t)s * KC), (lds_void *)(st + dst[i]),
+                                                 16, 0, 2);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(src[i] + (size_t)s * KC), (lds_void *)(st + dst[i]),
+                                                 16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < S) issue(p);
+    for (int s = 0; s < S; ++s) {
+        wait_stages<PW, NS - 2>(min(NS - 2, S - 1 - s));
+        lds_barrier();                               // stage s visible; slot (s-1)%NS free
+        if (s + NS - 1 < S) issue(s + NS - 1);
+    }
+}
+
+template <int BN, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT, bool ACC, bool GEN>
+__global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, const uint16_t *R, void *out, int M, int N, int K,
+    int n_tiles, int m_tiles, Epilogue ep) {
+    constexpr int NC = WK * WN * WM;
+    constexpr int NW = NL + NC;
+    static_assert(NW <= 16 && NL >= 1 && (!SPLIT || NL % 2 == 0), "wave layout");
+    static_assert(KC == 64 || KC == 128, "stage width");
+    static_assert((KC / 32) % WK == 0, "K steps per stage must split evenly over the K waves");
+    const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
+    constexpr int NT = NW * 64;
+    constexpr int RB = KC * 2;
+    constexpr int RPL = 1024 / RB;
+    constexpr int STAGE_BYTES = (BN + BM) * RB;
+    constexpr int WBLK = BN / RPL, XBLK = BM / RPL, BLOCKS = WBLK + XBLK;
+    static_assert(BN % RPL == 0 && BM % RPL == 0, "whole load blocks");
+    constexpr int NLW = SPLIT ? NL / 2 : NL;         // loaders that carry W rows
+    static_assert(SPLIT ? (WBLK % NLW == 0 && XBLK % (NL - NLW) == 0) : (WBLK % NL == 0 && XBLK % NL == 0),
+                  "load blocks must split evenly over the loaders");
+    constexpr int PWW = SPLIT ? WBLK / NLW : BLOCKS / NL;  // loads per stage of a W (or any) loader
+    constexpr int PWX = SPLIT ? XBLK / (NL - NLW) : PWW;   // of an X loader
+    static_assert(PWW * (NS - 2) < 64 && PWX * (NS - 2) < 64 && NS >= 2, "vmcnt budget");
+    constexpr int WNB = BN / WN, WMB = BM / WM;      // compute wave block
+    constexpr int TN = WNB / 16, TM = WMB / 16;
+    static_assert(TN >= 1 && TM >= 1 && WNB % 16 == 0 && WMB % 16 == 0, "wave block of whole tiles");
+    constexpr int KSTEPS = KC / 32 / WK;
+    constexpr int CP = BM + 4;
+    constexpr int CB = BN * CP;
+    constexpr int CBYTES = WK * CB * 4;
+    constexpr int LDS_BYTES = NS * STAGE_BYTES > CBYTES ? NS * STAGE_BYTES : CBYTES;
+    constexpr int EPT = BN * BM / NT;
+    static_assert(EPT * NT == BN * BM, "epilogue split");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    // block order as in the kernel above
+    const int b = blockIdx.x;
+    const int xcd = b & 7, j = b >> 3;
+    const int mt = j % m_tiles;
+    const int nt = (j / m_tiles) * 8 + xcd;
+    if (nt >= n_tiles) return;                       // padding block (uniform)
+    const int n0 = nt * BN, m0 = mt * BM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // a scalar role branch
+    const int S = K / KC;
+
+    uint16_t rv[EPT];                                // residual prefetch, as above
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid + NT * i;
+        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * epi.ldr + min(n0 + e % BN, N - 1)];
+    }
+
+    // Every wave meets the same S + 2 barriers: one per stage, one when the ring is done, one
+    // when the partial blocks are in LDS.
+    float *C = reinterpret_cast<float *>(lds);       // C[wk][n][m], row pitch CP
+    if (wave < NL) {
+        if constexpr (SPLIT) {
+            if (wave < NLW)
+                ring_loader<BN, BM, KC, NS, PWW, PWW>(X, W, M, N, K, n0, m0, lane, wave, NLW, lds, S);
+            else
+                ring_loader<BN, BM, KC, NS, PWX, 0>(X, W, M, N, K, n0, m0, lane, WBLK + wave - NLW, NL - NLW, lds,
+                                                    S);
+        } else {
+            ring_loader<BN, BM, KC, NS, PWW, WBLK / NL>(X, W, M, N, K, n0, m0, lane, wave, NL, lds, S);
+        }
+        __syncthreads();                             // (its waits cover every load of the ring)
+    } else {
+        const int cw = wave - NL;
+        const int wk = cw % WK, wn = ((cw / WK) % WN) * WNB, wm = (cw / (WK * WN)) * WMB;
+        f32x4_t acc[TN][TM];
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int c = 0; c < TM; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int frow = lane & 15, fq = lane >> 4;
+        for (int s = 0; s < S; ++s) {
+            // the fragment reads of the previous stage have returned (lgkmcnt 0) before the
+            // barrier that lets the loaders refill their slot
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            lds_barrier();
+            const uint8_t *Ws = lds + (s % NS) * STAGE_BYTES;
+            const uint8_t *Xs = Ws + BN * RB;
+#pragma unroll
+            for (int u = 0; u < KSTEPS; ++u) {
+                const int kk = u * WK + wk;
+                u32x4_t af[TN], bfr[TM];
+#pragma unroll
+                for (int a = 0; a < TN; ++a) {
+                    const int r = wn + 16 * a + frow;
+                    af[a] = *reinterpret_cast<const u32x4_t *>(Ws + r * RB + (((4 * kk + fq) ^ swizzle<RB>(r)) << 4));
+                }
+#pragma unroll
+                for (int c = 0; c < TM; ++c) {
+                    const int r = wm + 16 * c + frow;
+                    bfr[c] = *reinterpret_cast<const u32x4_t *>(Xs + r * RB + (((4 * kk + fq) ^ swizzle<RB>(r)) << 4));
+                }
+#pragma unroll
+                for (int a = 0; a < TN; ++a)
+#pragma unroll
+                    for (int c = 0; c < TM; ++c) acc[a][c] = mfma16(af[a], bfr[c], acc[a][c]);
+            }
+        }
+        __syncthreads();                             // every wave is done with the ring
+        float *Cw = C + wk * CB;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int c = 0; c < TM; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Cw[(wn + 16 * a + 4 * (lane >> 4) + r) * CP + wm + 16 * c + (lane & 15)] = acc[a][c][r];
+    }
+    __syncthreads();
+    // all waves finish the block: neighbouring threads take neighbouring n of one row of Y
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid + NT * i;
+        const int ml = e / BN, nl = e % BN;
+        const int m = m0 + ml, n = n0 + nl;
+        if (m < M && n < N) {
+            float t = C[nl * CP + ml];
+#pragma unroll
+            for (int q = 1; q < WK; ++q) t += C[q * CB + nl * CP + ml];
+            store_output<ACC>(out, epi, m, n, t, bf16_bits_to_f32(rv[i]));
+        }
+    }
+}
+
+template <int BN, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT>
+hipError_t launch_ring_ws(const LaunchArgs &a) {
+    const int n_tiles = (int)((a.N + BN - 1) / BN);
+    const int m_tiles = (int)((a.M + BM - 1) / BM);
+    const int groups = (n_tiles + 7) / 8;            // n-tiles per XCD, rounded up
+    dim3 grid((unsigned)(groups * 8 * m_tiles));
+    dim3 block((NL + WK * WN * WM) * 64);
+#define RING_ARGS a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep
+    if (a.acc_out)
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, true, true>), grid, block, 0,
+                           a.stream, RING_ARGS);
+    else if (plain_epilogue(a))
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, false>), grid, block, 0,
+                           a.stream, RING_ARGS);
+    else
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, true>), grid, block, 0,
+                           a.stream, RING_ARGS);
+#undef RING_ARGS
+    return hipGetLastError();
+}
+
 int64_t ring_max_k() { return INT64_MAX; }
 
 // Public knobs: path SKINNY_PATH_GEMM_RING, block_size = 64 * NW, outputs_per_block = BN,
@@ -260,6 +467,20 @@ int64_t ring_max_k() { return INT64_MAX; }
             &launch_ring<BN, BM, KC, NS, NW, WK, WN, WM>,                                             \
             (const void *)&mfma_ring_kernel<BN, BM, KC, NS, NW, WK, WN, WM, false, false>,            \
             (const void *)&mfma_ring_kernel<BN, BM, KC, NS, NW, WK, WN, WM, true, true>, &ring_max_k, KC \
+    }
+
+// Public knobs of the wave-specialised form: path SKINNY_PATH_GEMM_WS, block_size = 512 (4
+// loader and 4 compute waves), outputs_per_block = BN, k_unroll = NS, vector_width = 8 (every
+// loader takes W and X rows) or 9 (W rows and X rows on different loaders), m_tile = BM,
+// k_split = WK (compute waves taking alternate K steps of a stage; the others split the block,
+// two along W rows), k_stage = KC.
+#define WS_ENTRY(BN, BM, KC, NS, WK, SPLIT)                                                           \
+    KernelEntry {                                                                                     \
+        skinny_config{SKINNY_PATH_GEMM_WS, 512, BN, NS, (SPLIT) ? 9 : 8, BM, WK, KC},                 \
+            &launch_ring_ws<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT>,                               \
+            (const void *)&mfma_ring_ws_kernel<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, false, false>, \
+            (const void *)&mfma_ring_ws_kernel<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, true, true>,   \
+            &ring_max_k, KC                                                                           \
     }
 
 const KernelEntry kRingEntries[] = {
@@ -290,6 +511,25 @@ const KernelEntry kRingEntries[] = {
     RING_ENTRY(64, 128, 128, 3, 8, 4, 2, 1),
     RING_ENTRY(64, 128, 64, 5, 8, 1, 2, 4),
     RING_ENTRY(64, 192, 64, 4, 8, 2, 2, 2),
+    // wave-specialised form
+    WS_ENTRY(32, 32, 128, 4, 1, false),
+    WS_ENTRY(32, 32, 128, 5, 2, false),
+    WS_ENTRY(32, 48, 128, 4, 2, false),
+    WS_ENTRY(32, 64, 128, 4, 1, false),
+    WS_ENTRY(32, 64, 128, 4, 1, true),
+    WS_ENTRY(32, 64, 128, 5, 1, false),
+    WS_ENTRY(32, 80, 128, 4, 2, false),
+    WS_ENTRY(32, 80, 128, 4, 2, true),
+    WS_ENTRY(32, 96, 128, 4, 1, true),
+    WS_ENTRY(64, 64, 128, 4, 1, false),
+    WS_ENTRY(64, 64, 128, 4, 1, true),
+    WS_ENTRY(64, 64, 128, 5, 1, true),
+    WS_ENTRY(64, 64, 128, 4, 2, true),
+    WS_ENTRY(64, 96, 128, 3, 1, false),
+    WS_ENTRY(64, 96, 128, 3, 1, true),
+    WS_ENTRY(64, 128, 128, 3, 1, false),
+    WS_ENTRY(64, 128, 128, 3, 1, true),
+    WS_ENTRY(64, 128, 128, 3, 2, false),
 };
 
 }  // namespace

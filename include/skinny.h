@@ -72,10 +72,16 @@ enum {
                                  k_split 4: the 4 waves split each stage's K steps, 1: they
                                  split the output block); K must be a multiple of 128 (else
                                  SKINNY_ENOTSUP) */
-    SKINNY_PATH_GEMM_RING = 6 /* the same operand pipeline with k_stage-wide stages (64 or 128)
+    SKINNY_PATH_GEMM_RING = 6, /* the same operand pipeline with k_stage-wide stages (64 or 128)
                                  and 4 or 8 waves (block_size 256 or 512); k_split = waves
                                  taking alternate K steps of a stage, the others split the
                                  block; K must be a multiple of k_stage (else SKINNY_ENOTSUP) */
+    SKINNY_PATH_GEMM_WS = 7   /* the ring of SKINNY_PATH_GEMM_RING with wave-specialised roles:
+                                 4 waves only load the stages, 4 only run the matrix
+                                 instructions (block_size 512); k_split = compute waves taking
+                                 alternate K steps; vector_width 8 = each loading wave takes W
+                                 and X rows, 9 = W rows and X rows on different waves; K must be
+                                 a multiple of k_stage (else SKINNY_ENOTSUP) */
 };
 
 /*
@@ -93,14 +99,15 @@ typedef struct skinny_config {
                                   4 (8 B). GEMV and MFMA_LDS encode their row order here:
                                   8 = rows strided over the grid, 9 = contiguous rows per
                                   workgroup, 10 (MFMA_LDS) = contiguous with X loaded first;
-                                  all three load 16 B */
+                                  all three load 16 B. GEMM_WS encodes its loader roles here
+                                  (8 or 9, see SKINNY_PATH_GEMM_WS) */
     int32_t m_tile;            /* rows of X handled per pass (compile-time tile); M larger
                                   than m_tile runs ceil(M / m_tile) passes; 0 = let the
                                   library pick the smallest built tile >= M */
     int32_t k_split;           /* waves of a workgroup that share the same output columns
                                   and split K between them (their partial sums meet in LDS) */
-    int32_t k_stage;           /* K per LDS stage of SKINNY_PATH_GEMM_RING (64 or 128); 0 for
-                                  every other path */
+    int32_t k_stage;           /* K per LDS stage of SKINNY_PATH_GEMM_RING and _GEMM_WS (64 or
+                                  128); 0 for every other path */
 } skinny_config;
 
 /*

@@ -51,7 +51,7 @@ def refuses(cfg, K):
     return ((cfg["path"] == 0 and K > cfg["k_unroll"] * cfg["k_split"] * 512) or
             (cfg["path"] == 2 and K > cfg["k_split"] * 512) or
             (cfg["path"] == 5 and K % 128 != 0) or
-            (cfg["path"] == 6 and K % cfg["k_stage"] != 0))
+            (cfg["path"] in (6, 7) and K % cfg["k_stage"] != 0))
 
 
 def all_configs(sk, K=None):
@@ -134,7 +134,7 @@ def test_matrix_core_configs_full_size_sampled(sk, M):
     ms, ns = sample_positions(M, N_FULL, 2000, 200 + M)
     yo, ao = oracle.addmm_bf16_points(synth.bits(X), synth.bits(ws[0]), synth.bits(rs[0]), ms, ns)
     for cfg in all_configs(sk, K_FULL):
-        if cfg["path"] not in (1, 3, 5, 6):
+        if cfg["path"] not in (1, 3, 5, 6, 7):
             continue
         print("full size M=%d config %s" % (M, cfg), flush=True)
         Yg, Ag = run_both(sk, X, ws[0], rs[0], cfg)
