@@ -80,12 +80,19 @@ skinny_config table_row(int64_t M, int64_t N) {
 }
 
 // The table's choice for (M, N), unless that kernel cannot take this K (GEMV instances hold
-// their K slice in registers; the direct-to-LDS GEMM needs whole 128-wide K stages); then
-// the general configuration for that M range, which takes any K.
+// their K slice in registers; the direct-to-LDS GEMMs need whole K stages); then a second
+// choice for the M range if it can (the LDS-MFMA kernel for M <= 16: any K up to its on-chip
+// slice; 128-wide stages above), else the general configuration for that M range, which takes
+// any K.
 skinny_config select(int64_t M, int64_t N, int64_t K) {
+    auto takes = [&](const skinny_config &c) {
+        const KernelEntry *e = find_entry(c, M);
+        return e && K <= e->max_k() && K % e->k_align == 0;
+    };
     const skinny_config c = table_row(M, N);
-    const KernelEntry *e = find_entry(c, M);
-    if (e && K <= e->max_k() && K % e->k_align == 0) return c;
+    if (takes(c)) return c;
+    if (M <= 16 && takes(kSecondSmall)) return kSecondSmall;
+    if (M > 16 && takes(kSecondLarge)) return kSecondLarge;
     return M <= 16 ? kFallbackSmall : kFallbackLarge;
 }
 
@@ -170,8 +177,9 @@ skinny_status run(const void *X, const void *W, const void *R, int64_t ldr, void
     if (c.block_size <= 0 || c.block_size % 64 != 0 || c.outputs_per_block <= 0 ||
         c.k_unroll <= 0 || c.vector_width < 4 || c.vector_width > 10 || c.m_tile < 0 ||
         c.k_split <= 0 || (c.block_size / 64) % c.k_split != 0 ||
-        ((c.path == SKINNY_PATH_GEMM_RING || c.path == SKINNY_PATH_GEMM_WS) ? (c.k_stage != 64 && c.k_stage != 128)
-                                                                           : c.k_stage != 0))
+        (c.path == SKINNY_PATH_GEMM_RING ? (c.k_stage != 64 && c.k_stage != 128)
+         : c.path == SKINNY_PATH_GEMM_WS ? (c.k_stage != 64 && c.k_stage != 128 && c.k_stage != 256)
+                                          : c.k_stage != 0))
         return SKINNY_EINVAL;
     const KernelEntry *e = find_entry(c, M);
     if (!e) return SKINNY_ENOTSUP;

@@ -16,8 +16,9 @@
 //   * each stage is (BN + BM) rows in LDS, filled by direct-to-LDS loads (16 bytes per lane,
 //     1 KB per instruction), W rows non-temporal, X rows with the default policy;
 //   * 16-byte chunks are XOR-swizzled so the 16-row fragment reads of v_mfma_f32_16x16x32_bf16
-//     hit 16 distinct bank groups: chunk c of row r at c ^ (r & 15) for 256-byte rows,
-//     c ^ ((r >> 1) & 7) for 128-byte rows (rows r and r + 1 share a 256-byte bank window);
+//     hit 16 distinct bank groups: chunk c of row r at c ^ (r & 15) for 256-byte rows (and the
+//     512-byte rows of the wave-specialised form), c ^ ((r >> 1) & 7) for 128-byte rows (rows r
+//     and r + 1 share a 256-byte bank window);
 //   * each wave waits for its own loads of a stage with an explicit vmcnt, then one barrier
 //     publishes the stage and frees the slot read one iteration earlier, which is refilled;
 //   * R is fetched into registers before the K loop; the epilogue stages the block in LDS,
@@ -74,7 +75,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int RB>
 __device__ __forceinline__ int swizzle(int r) {
-    return RB == 256 ? (r & 15) : ((r >> 1) & 7);
+    return RB >= 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // BN, BM: rows of W and of X per block; KC: K per stage; NS: ring stages; NW waves laid out
@@ -311,7 +312,7 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     constexpr int NC = WK * WN * WM;
     constexpr int NW = NL + NC;
     static_assert(NW <= 16 && NL >= 1 && (!SPLIT || NL % 2 == 0), "wave layout");
-    static_assert(KC == 64 || KC == 128, "stage width");
+    static_assert(KC == 64 || KC == 128 || KC == 256, "stage width");
     static_assert((KC / 32) % WK == 0, "K steps per stage must split evenly over the K waves");
     const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
     constexpr int NT = NW * 64;
@@ -473,7 +474,7 @@ int64_t ring_max_k() { return INT64_MAX; }
 // loader and 4 compute waves), outputs_per_block = BN, k_unroll = NS, vector_width = 8 (every
 // loader takes W and X rows) or 9 (W rows and X rows on different loaders), m_tile = BM,
 // k_split = WK (compute waves taking alternate K steps of a stage; the others split the block,
-// two along W rows), k_stage = KC.
+// two along W rows), k_stage = KC (64, 128 or 256: 128-, 256- or 512-byte row pieces).
 #define WS_ENTRY(BN, BM, KC, NS, WK, SPLIT)                                                           \
     KernelEntry {                                                                                     \
         skinny_config{SKINNY_PATH_GEMM_WS, 512, BN, NS, (SPLIT) ? 9 : 8, BM, WK, KC},                 \
@@ -512,12 +513,15 @@ const KernelEntry kRingEntries[] = {
     RING_ENTRY(64, 128, 64, 5, 8, 1, 2, 4),
     RING_ENTRY(64, 192, 64, 4, 8, 2, 2, 2),
     // wave-specialised form
+    WS_ENTRY(32, 16, 128, 6, 2, false),
     WS_ENTRY(32, 32, 128, 4, 1, false),
     WS_ENTRY(32, 32, 128, 5, 2, false),
     WS_ENTRY(32, 48, 128, 4, 2, false),
+    WS_ENTRY(32, 48, 256, 3, 2, false),
     WS_ENTRY(32, 64, 128, 4, 1, false),
     WS_ENTRY(32, 64, 128, 4, 1, true),
     WS_ENTRY(32, 64, 128, 5, 1, false),
+    WS_ENTRY(32, 64, 256, 3, 1, false),
     WS_ENTRY(32, 80, 128, 4, 2, false),
     WS_ENTRY(32, 80, 128, 4, 2, true),
     WS_ENTRY(32, 96, 128, 4, 1, true),

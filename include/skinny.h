@@ -106,8 +106,8 @@ typedef struct skinny_config {
                                   library pick the smallest built tile >= M */
     int32_t k_split;           /* waves of a workgroup that share the same output columns
                                   and split K between them (their partial sums meet in LDS) */
-    int32_t k_stage;           /* K per LDS stage of SKINNY_PATH_GEMM_RING and _GEMM_WS (64 or
-                                  128); 0 for every other path */
+    int32_t k_stage;           /* K per LDS stage of SKINNY_PATH_GEMM_RING (64 or 128) and
+                                  SKINNY_PATH_GEMM_WS (64, 128 or 256); 0 for every other path */
 } skinny_config;
 
 /*

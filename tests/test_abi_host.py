@@ -73,6 +73,21 @@ def test_table_rows_resolve_without_fallback(L, N):
         assert c.as_dict()["path"] not in (1, 3), (M, N, c.as_dict())
 
 
+@pytest.mark.parametrize("M,K,path,k_stage", [
+    (8, 1032, 2, 0),        # not a whole number of 128-wide stages: LDS-MFMA (any K up to 3584)
+    (8, 4104, 1, 0),        # beyond the LDS-MFMA slice as well: the direct MFMA fallback
+    (48, 3712, 7, 128),     # not a whole number of 256-wide stages: 128-wide ones
+    (48, 1032, 3, 0),       # neither: the register GEMM fallback
+])
+def test_second_choice_when_the_row_cannot_take_k(L, M, K, path, k_stage):
+    """A table row whose kernel cannot take K gives way to the M range's second choice before
+    the general fallback."""
+    c = _lib.SkinnyConfig()
+    assert L.skinny_select_config(M, 7168, K, ctypes.byref(c)) == 0
+    d = c.as_dict()
+    assert (d["path"], d["k_stage"]) == (path, k_stage), d
+
+
 ENV_PROBE = r"""
 import ctypes, json, sys
 sys.path.insert(0, sys.argv[1])

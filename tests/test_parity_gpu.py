@@ -144,10 +144,12 @@ def test_matrix_core_configs_full_size_sampled(sk, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 300, 4104), (4, 256, 8), (16, 200, 9000), (64, 130, 24),
-                                   (300, 1000, 1032), (257, 515, 3584), (33, 70, 512)])
+                                   (300, 1000, 1032), (257, 515, 3584), (33, 70, 512),
+                                   (8, 300, 1032), (48, 300, 3712)])
 def test_selected_config_any_shape(sk, M, N, K):
-    """The library's own choice (tuned table, with its fallbacks for other K) at shapes off the
-    tuned one: ragged N, K outside a kernel's on-chip slice, M above the table."""
+    """The library's own choice (tuned table, with its second choices and fallbacks for other K)
+    at shapes off the tuned one: ragged N, K outside a kernel's on-chip slice or not a whole
+    number of its stages, M above the table."""
     X, ws, rs = synth.make_inputs(M, N, K, seed=M + N + K)
     print("selected config", (M, N, K), sk.select_config(M, N, K), flush=True)
     Xd, Wd, Rd = _dev(X, ws[0], rs[0])
