@@ -100,7 +100,7 @@ def sample_positions(M, N, count, seed):
     return np.array(ms, np.int64), np.array(ns, np.int64)
 
 
-@pytest.mark.parametrize("M", [17, 26, 32, 48, 64, 80, 128, 256])
+@pytest.mark.parametrize("M", [17, 26, 32, 40, 41, 48, 64, 80, 96, 97, 128, 160, 192, 208, 256])
 def test_full_size_full_oracle_large_m(sk, M):
     """Every table row above M = 16 (and the M just past each boundary) at the full N x K
     problem: every output against the oracle, at the selected configuration."""
