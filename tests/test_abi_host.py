@@ -73,6 +73,22 @@ def test_table_rows_resolve_without_fallback(L, N):
         assert c.as_dict()["path"] not in (1, 3), (M, N, c.as_dict())
 
 
+def test_full_oracle_parity_reaches_every_selected_config(L):
+    """Every configuration the table selects at N = 7168, K = 3584 for M = 1 ... 300 is one that
+    the full-output GPU parity tests run (their M lists live in parity.py), so a new or changed
+    table row cannot go without a full comparison with the oracle."""
+    import parity as P
+
+    def sel(M):
+        c = _lib.SkinnyConfig()
+        assert L.skinny_select_config(M, 7168, 3584, ctypes.byref(c)) == 0
+        return tuple(c.as_dict().values())
+
+    tested = {sel(M) for M in P.FULL_ORACLE_SMALL_M + P.FULL_ORACLE_LARGE_M}
+    missing = {(M, sel(M)) for M in range(1, 301) if sel(M) not in tested}
+    assert not missing, sorted(missing)[:5]
+
+
 @pytest.mark.parametrize("M,K,path,k_stage", [
     (8, 1032, 2, 0),        # not a whole number of 128-wide stages: LDS-MFMA (any K up to 3584)
     (8, 4104, 1, 0),        # beyond the LDS-MFMA slice as well: the direct MFMA fallback

@@ -75,7 +75,7 @@ def test_small_shapes_every_config(sk):
             assert np.array_equal(Yg.reshape(-1), P.rne_torch(Ag).reshape(-1)), "Y != RNE(ACC)"
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("M", P.FULL_ORACLE_SMALL_M)
 def test_full_size_full_oracle(sk, M):
     """Full N x K problem, every output against the oracle, at the selected configuration."""
     X, ws, rs = synth.make_inputs(M, N_FULL, K_FULL)
@@ -100,7 +100,7 @@ def sample_positions(M, N, count, seed):
     return np.array(ms, np.int64), np.array(ns, np.int64)
 
 
-@pytest.mark.parametrize("M", [17, 26, 32, 40, 41, 48, 64, 80, 96, 97, 128, 160, 192, 208, 256])
+@pytest.mark.parametrize("M", P.FULL_ORACLE_LARGE_M)
 def test_full_size_full_oracle_large_m(sk, M):
     """Every table row above M = 16 (and the M just past each boundary) at the full N x K
     problem: every output against the oracle, at the selected configuration."""
