@@ -263,23 +263,24 @@ hipError_t launch_ring(const LaunchArgs &a) {
 // stage's load blocks NL*i + lw.
 //
 // One loader's part of the ring: PW load blocks (1 KB) per stage, block q = first + step*i
-// holding rows RPL*q ... of the stage (its W rows first, then its X rows); the first NWI of
-// them are W rows and carry the non-temporal policy. Lane l fills position l of a block, as in
-// the kernel above.
-template <int BN, int BM, int KC, int NS, int PW, int NWI>
+// holding rows RPL*q ... of the stage (its BNV W rows first, then its BM X rows); the first NWI
+// of them are W rows and carry the non-temporal policy. Lane l fills position l of a block, as
+// in the kernel above.
+template <int BNV, int BM, int KC, int NS, int PW, int NWI>
 __device__ __forceinline__ void ring_loader(const uint16_t *X, const uint16_t *W, int M, int N, int K, int n0,
                                             int m0, int lane, int first, int step, uint8_t *lds, int S) {
     constexpr int RB = KC * 2, CPR = RB / 16, RPL = 1024 / RB;
-    constexpr int STAGE_BYTES = (BN + BM) * RB;
+    constexpr int STAGE_BYTES = (BNV + BM) * RB;
     const uint16_t *src[PW];
     int dst[PW];
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
         const int q = first + step * i;
-        const int sr = RPL * q + lane / CPR;
-        const int c = (lane % CPR) ^ swizzle<RB>(sr);
-        const uint16_t *row = sr < BN ? W + (size_t)min(n0 + sr, N - 1) * K
-                                      : X + (size_t)min(m0 + sr - BN, M - 1) * K;
+        const int sr = RPL * q + lane / CPR;         // row of the stage
+        const int orow = sr < BNV ? sr : sr - BNV;   // row of its operand (the swizzle's row)
+        const int c = (lane % CPR) ^ swizzle<RB>(orow);
+        const uint16_t *row = sr < BNV ? W + (size_t)min(n0 + sr, N - 1) * K
+                                       : X + (size_t)min(m0 + orow, M - 1) * K;
         src[i] = row + 8 * c;
         dst[i] = q * 1024;
     }
@@ -305,27 +306,49 @@ __device__ __forceinline__ void ring_loader(const uint16_t *X, const uint16_t *W
     }
 }
 
-template <int BN, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT, bool ACC, bool GEN>
+// The loaders of one role (W rows or X rows of a stage, SPLIT form): `blocks` load blocks from
+// block `base` on, dealt round-robin over `count` loaders; when they do not split evenly the
+// first blocks % count loaders take one more. Each loader's count is a compile-time constant,
+// so its vmcnt waits count exactly its own loads.
+template <int BNV, int BM, int KC, int NS, int BLOCKS, int COUNT, bool WROWS>
+__device__ __forceinline__ void ring_loader_role(const uint16_t *X, const uint16_t *W, int M, int N, int K, int n0,
+                                                 int m0, int lane, int idx, int base, uint8_t *lds, int S) {
+    constexpr int PH = (BLOCKS + COUNT - 1) / COUNT, REM = BLOCKS % COUNT;
+    static_assert(BLOCKS >= COUNT, "every loader of the role has a block");
+    if (REM == 0 || idx < REM)
+        ring_loader<BNV, BM, KC, NS, PH, WROWS ? PH : 0>(X, W, M, N, K, n0, m0, lane, base + idx, COUNT, lds, S);
+    else
+        ring_loader<BNV, BM, KC, NS, PH - 1, WROWS ? PH - 1 : 0>(X, W, M, N, K, n0, m0, lane, base + idx, COUNT,
+                                                                 lds, S);
+}
+
+// BN: W rows of the matrix-instruction block; BNV <= BN of them are a block's own (loaded,
+// finished and stored): with BNV = 7/8 BN, N = 7168 splits into 256 blocks of 28 or 128 of 56
+// W rows, one or two per compute unit, instead of 224 or 112. Fragment reads of the rows past
+// BNV land on X rows of the same stage; their results are never stored.
+template <int BN, int BNV, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT, bool ACC, bool GEN>
 __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, const uint16_t *R, void *out, int M, int N, int K,
     int n_tiles, int m_tiles, Epilogue ep) {
     constexpr int NC = WK * WN * WM;
     constexpr int NW = NL + NC;
     static_assert(NW <= 16 && NL >= 1 && (!SPLIT || NL % 2 == 0), "wave layout");
+    static_assert(BNV <= BN && BN - BNV <= BM, "fragment reads stay inside the stage");
     static_assert(KC == 64 || KC == 128 || KC == 256, "stage width");
     static_assert((KC / 32) % WK == 0, "K steps per stage must split evenly over the K waves");
     const Epilogue epi = GEN ? ep : Epilogue{N, N, 0u};  // see plain_epilogue
     constexpr int NT = NW * 64;
     constexpr int RB = KC * 2;
     constexpr int RPL = 1024 / RB;
-    constexpr int STAGE_BYTES = (BN + BM) * RB;
-    constexpr int WBLK = BN / RPL, XBLK = BM / RPL, BLOCKS = WBLK + XBLK;
-    static_assert(BN % RPL == 0 && BM % RPL == 0, "whole load blocks");
+    constexpr int STAGE_BYTES = (BNV + BM) * RB;
+    constexpr int WBLK = BNV / RPL, XBLK = BM / RPL, BLOCKS = WBLK + XBLK;
+    static_assert(BNV % RPL == 0 && BM % RPL == 0, "whole load blocks");
     constexpr int NLW = SPLIT ? NL / 2 : NL;         // loaders that carry W rows
-    static_assert(SPLIT ? (WBLK % NLW == 0 && XBLK % (NL - NLW) == 0) : (WBLK % NL == 0 && XBLK % NL == 0),
-                  "load blocks must split evenly over the loaders");
-    constexpr int PWW = SPLIT ? WBLK / NLW : BLOCKS / NL;  // loads per stage of a W (or any) loader
-    constexpr int PWX = SPLIT ? XBLK / (NL - NLW) : PWW;   // of an X loader
+    static_assert(SPLIT || (WBLK % NL == 0 && XBLK % NL == 0), "load blocks must split evenly over the loaders");
+    // most loads per stage of a W (or any) loader and of an X loader (SPLIT: one fewer for the
+    // last loaders of a role when its blocks do not split evenly)
+    constexpr int PWW = SPLIT ? (WBLK + NLW - 1) / NLW : BLOCKS / NL;
+    constexpr int PWX = SPLIT ? (XBLK + NL - NLW - 1) / (NL - NLW) : PWW;
     static_assert(PWW * (NS - 2) < 64 && PWX * (NS - 2) < 64 && NS >= 2, "vmcnt budget");
     constexpr int WNB = BN / WN, WMB = BM / WM;      // compute wave block
     constexpr int TN = WNB / 16, TM = WMB / 16;
@@ -338,8 +361,8 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     // no barrier has to separate the last fragment reads from their writes (0.1 us at M >= 32)
     constexpr bool CSEP = NS * STAGE_BYTES + CBYTES <= 160 * 1024;
     constexpr int LDS_BYTES = CSEP ? NS * STAGE_BYTES + CBYTES : (NS * STAGE_BYTES > CBYTES ? NS * STAGE_BYTES : CBYTES);
-    constexpr int EPT = BN * BM / NT;
-    static_assert(EPT * NT == BN * BM, "epilogue split");
+    constexpr int OUTS = BNV * BM;                  // outputs of a block
+    constexpr int EPT = (OUTS + NT - 1) / NT;        // finished per thread (the last round ragged)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     // block order as in the kernel above
@@ -348,7 +371,7 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     const int mt = j % m_tiles;
     const int nt = (j / m_tiles) * 8 + xcd;
     if (nt >= n_tiles) return;                       // padding block (uniform)
-    const int n0 = nt * BN, m0 = mt * BM;
+    const int n0 = nt * BNV, m0 = mt * BM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -359,7 +382,7 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid + NT * i;
-        rv[i] = R[(size_t)min(m0 + e / BN, M - 1) * epi.ldr + min(n0 + e % BN, N - 1)];
+        rv[i] = R[(size_t)min(m0 + e / BNV, M - 1) * epi.ldr + min(n0 + e % BNV, N - 1)];
     }
 
     // Every wave meets the same barriers: one per stage, one when the ring is done (unless the
@@ -368,12 +391,12 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     if (wave < NL) {
         if constexpr (SPLIT) {
             if (wave < NLW)
-                ring_loader<BN, BM, KC, NS, PWW, PWW>(X, W, M, N, K, n0, m0, lane, wave, NLW, lds, S);
+                ring_loader_role<BNV, BM, KC, NS, WBLK, NLW, true>(X, W, M, N, K, n0, m0, lane, wave, 0, lds, S);
             else
-                ring_loader<BN, BM, KC, NS, PWX, 0>(X, W, M, N, K, n0, m0, lane, WBLK + wave - NLW, NL - NLW, lds,
-                                                    S);
+                ring_loader_role<BNV, BM, KC, NS, XBLK, NL - NLW, false>(X, W, M, N, K, n0, m0, lane, wave - NLW,
+                                                                         WBLK, lds, S);
         } else {
-            ring_loader<BN, BM, KC, NS, PWW, WBLK / NL>(X, W, M, N, K, n0, m0, lane, wave, NL, lds, S);
+            ring_loader<BNV, BM, KC, NS, PWW, WBLK / NL>(X, W, M, N, K, n0, m0, lane, wave, NL, lds, S);
         }
         if (!CSEP) __syncthreads();                  // (its waits cover every load of the ring)
     } else {
@@ -391,7 +414,7 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
             __builtin_amdgcn_s_waitcnt(0xC07F);
             lds_barrier();
             const uint8_t *Ws = lds + (s % NS) * STAGE_BYTES;
-            const uint8_t *Xs = Ws + BN * RB;
+            const uint8_t *Xs = Ws + BNV * RB;
 #pragma unroll
             for (int u = 0; u < KSTEPS; ++u) {
                 const int kk = u * WK + wk;
@@ -427,9 +450,9 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid + NT * i;
-        const int ml = e / BN, nl = e % BN;
+        const int ml = e / BNV, nl = e % BNV;
         const int m = m0 + ml, n = n0 + nl;
-        if (m < M && n < N) {
+        if ((OUTS % NT == 0 || e < OUTS) && m < M && n < N) {
             float t = C[nl * CP + ml];
 #pragma unroll
             for (int q = 1; q < WK; ++q) t += C[q * CB + nl * CP + ml];
@@ -438,22 +461,22 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     }
 }
 
-template <int BN, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT>
+template <int BN, int BNV, int BM, int KC, int NS, int NL, int WK, int WN, int WM, bool SPLIT>
 hipError_t launch_ring_ws(const LaunchArgs &a) {
-    const int n_tiles = (int)((a.N + BN - 1) / BN);
+    const int n_tiles = (int)((a.N + BNV - 1) / BNV);
     const int m_tiles = (int)((a.M + BM - 1) / BM);
     const int groups = (n_tiles + 7) / 8;            // n-tiles per XCD, rounded up
     dim3 grid((unsigned)(groups * 8 * m_tiles));
     dim3 block((NL + WK * WN * WM) * 64);
 #define RING_ARGS a.X, a.W, a.R, a.out, (int)a.M, (int)a.N, (int)a.K, n_tiles, m_tiles, a.ep
     if (a.acc_out)
-        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, true, true>), grid, block, 0,
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BNV, BM, KC, NS, NL, WK, WN, WM, SPLIT, true, true>), grid, block, 0,
                            a.stream, RING_ARGS);
     else if (plain_epilogue(a))
-        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, false>), grid, block, 0,
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BNV, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, false>), grid, block, 0,
                            a.stream, RING_ARGS);
     else
-        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, true>), grid, block, 0,
+        hipLaunchKernelGGL((mfma_ring_ws_kernel<BN, BNV, BM, KC, NS, NL, WK, WN, WM, SPLIT, false, true>), grid, block, 0,
                            a.stream, RING_ARGS);
 #undef RING_ARGS
     return hipGetLastError();
@@ -478,14 +501,15 @@ int64_t ring_max_k() { return INT64_MAX; }
 // loader takes W and X rows) or 9 (W rows and X rows on different loaders), m_tile = BM,
 // k_split = WK (compute waves taking alternate K steps of a stage; the others split the block,
 // two along W rows), k_stage = KC (64, 128 or 256: 128-, 256- or 512-byte row pieces).
-#define WS_ENTRY(BN, BM, KC, NS, WK, SPLIT)                                                           \
+#define WS_ENTRY_V(BN, BNV, BM, KC, NS, WK, SPLIT)                                                    \
     KernelEntry {                                                                                     \
-        skinny_config{SKINNY_PATH_GEMM_WS, 512, BN, NS, (SPLIT) ? 9 : 8, BM, WK, KC},                 \
-            &launch_ring_ws<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT>,                               \
-            (const void *)&mfma_ring_ws_kernel<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, false, false>, \
-            (const void *)&mfma_ring_ws_kernel<BN, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, true, true>,   \
+        skinny_config{SKINNY_PATH_GEMM_WS, 512, BNV, NS, (SPLIT) ? 9 : 8, BM, WK, KC},                \
+            &launch_ring_ws<BN, BNV, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT>,                          \
+            (const void *)&mfma_ring_ws_kernel<BN, BNV, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, false, false>, \
+            (const void *)&mfma_ring_ws_kernel<BN, BNV, BM, KC, NS, 4, WK, 2, 2 / (WK), SPLIT, true, true>,   \
             &ring_max_k, KC                                                                           \
     }
+#define WS_ENTRY(BN, BM, KC, NS, WK, SPLIT) WS_ENTRY_V(BN, BN, BM, KC, NS, WK, SPLIT)
 
 const KernelEntry kRingEntries[] = {
     // 32 W rows per block (224 workgroups at N = 7168)
@@ -537,6 +561,17 @@ const KernelEntry kRingEntries[] = {
     WS_ENTRY(64, 128, 128, 3, 1, false),
     WS_ENTRY(64, 128, 128, 3, 1, true),
     WS_ENTRY(64, 128, 128, 3, 2, false),
+    // 7/8 of the matrix block's W rows per block: 256 (28 rows) or 128 (56 rows) blocks at N = 7168
+    WS_ENTRY_V(32, 28, 16, 128, 6, 2, true),
+    WS_ENTRY_V(32, 28, 16, 256, 4, 2, true),
+    WS_ENTRY_V(32, 28, 32, 128, 5, 2, true),
+    WS_ENTRY_V(32, 28, 32, 256, 4, 2, true),
+    WS_ENTRY_V(32, 28, 48, 128, 4, 2, true),
+    WS_ENTRY_V(32, 28, 64, 256, 3, 1, true),
+    WS_ENTRY_V(32, 28, 80, 128, 4, 2, true),
+    WS_ENTRY_V(64, 56, 64, 128, 4, 1, true),
+    WS_ENTRY_V(64, 56, 96, 128, 3, 1, true),
+    WS_ENTRY_V(64, 56, 128, 128, 3, 1, true),
 };
 
 }  // namespace
