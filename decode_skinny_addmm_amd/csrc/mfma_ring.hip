@@ -322,6 +322,24 @@ __device__ __forceinline__ void ring_loader_role(const uint16_t *X, const uint16
                                                                  lds, S);
 }
 
+// Mixed form with load blocks that do not split evenly: loader w takes blocks w, w + NL, ...
+// of the stage (W blocks first), so its load count and how many of them are W rows are
+// compile-time constants of w; one instance per loader.
+template <int BNV, int BM, int KC, int NS, int NL, int WBLK, int BLOCKS, int LW>
+__device__ __forceinline__ void ring_loader_mixed(const uint16_t *X, const uint16_t *W, int M, int N, int K, int n0,
+                                                  int m0, int lane, int wave, uint8_t *lds, int S) {
+    if constexpr (LW < NL) {
+        if (wave == LW) {
+            constexpr int PW = (BLOCKS - LW + NL - 1) / NL;
+            constexpr int NWI = WBLK > LW ? (WBLK - LW + NL - 1) / NL : 0;
+            static_assert(PW >= 1, "every loader has a block");
+            ring_loader<BNV, BM, KC, NS, PW, NWI>(X, W, M, N, K, n0, m0, lane, LW, NL, lds, S);
+        } else {
+            ring_loader_mixed<BNV, BM, KC, NS, NL, WBLK, BLOCKS, LW + 1>(X, W, M, N, K, n0, m0, lane, wave, lds, S);
+        }
+    }
+}
+
 // BN: W rows of the matrix-instruction block; BNV <= BN of them are a block's own (loaded,
 // finished and stored): with BNV = 7/8 BN, N = 7168 splits into 256 blocks of 28 or 128 of 56
 // W rows, one or two per compute unit, instead of 224 or 112. Fragment reads of the rows past
@@ -344,10 +362,10 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     constexpr int WBLK = BNV / RPL, XBLK = BM / RPL, BLOCKS = WBLK + XBLK;
     static_assert(BNV % RPL == 0 && BM % RPL == 0, "whole load blocks");
     constexpr int NLW = SPLIT ? NL / 2 : NL;         // loaders that carry W rows
-    static_assert(SPLIT || (WBLK % NL == 0 && XBLK % NL == 0), "load blocks must split evenly over the loaders");
-    // most loads per stage of a W (or any) loader and of an X loader (SPLIT: one fewer for the
-    // last loaders of a role when its blocks do not split evenly)
-    constexpr int PWW = SPLIT ? (WBLK + NLW - 1) / NLW : BLOCKS / NL;
+    constexpr bool EVEN = WBLK % NL == 0 && XBLK % NL == 0;  // mixed form: every loader alike
+    // most loads per stage of a W (or any) loader and of an X loader (one fewer for the last
+    // loaders of a role, or of the mixed form, when the blocks do not split evenly)
+    constexpr int PWW = SPLIT ? (WBLK + NLW - 1) / NLW : (BLOCKS + NL - 1) / NL;
     constexpr int PWX = SPLIT ? (XBLK + NL - NLW - 1) / (NL - NLW) : PWW;
     static_assert(PWW * (NS - 2) < 64 && PWX * (NS - 2) < 64 && NS >= 2, "vmcnt budget");
     constexpr int WNB = BN / WN, WMB = BM / WM;      // compute wave block
@@ -395,8 +413,10 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
             else
                 ring_loader_role<BNV, BM, KC, NS, XBLK, NL - NLW, false>(X, W, M, N, K, n0, m0, lane, wave - NLW,
                                                                          WBLK, lds, S);
-        } else {
+        } else if constexpr (EVEN) {
             ring_loader<BNV, BM, KC, NS, PWW, WBLK / NL>(X, W, M, N, K, n0, m0, lane, wave, NL, lds, S);
+        } else {
+            ring_loader_mixed<BNV, BM, KC, NS, NL, WBLK, BLOCKS, 0>(X, W, M, N, K, n0, m0, lane, wave, lds, S);
         }
         if (!CSEP) __syncthreads();                  // (its waits cover every load of the ring)
     } else {
@@ -572,6 +592,15 @@ const KernelEntry kRingEntries[] = {
     WS_ENTRY_V(64, 56, 64, 128, 4, 1, true),
     WS_ENTRY_V(64, 56, 96, 128, 3, 1, true),
     WS_ENTRY_V(64, 56, 128, 128, 3, 1, true),
+    WS_ENTRY_V(32, 28, 16, 128, 6, 2, false),
+    WS_ENTRY_V(32, 28, 32, 128, 5, 2, false),
+    WS_ENTRY_V(32, 28, 48, 128, 4, 2, false),
+    WS_ENTRY_V(32, 28, 80, 128, 4, 2, false),
+    WS_ENTRY_V(64, 56, 64, 128, 4, 1, false),
+    WS_ENTRY_V(64, 56, 128, 128, 3, 1, false),
+    WS_ENTRY_V(32, 28, 64, 128, 4, 1, false),
+    WS_ENTRY_V(32, 28, 64, 128, 4, 2, false),
+    WS_ENTRY_V(32, 28, 64, 256, 3, 1, false),
 };
 
 }  // namespace
