@@ -601,6 +601,9 @@ const KernelEntry kRingEntries[] = {
     WS_ENTRY_V(32, 28, 64, 128, 4, 1, false),
     WS_ENTRY_V(32, 28, 64, 128, 4, 2, false),
     WS_ENTRY_V(32, 28, 64, 256, 3, 1, false),
+    WS_ENTRY_V(64, 56, 80, 128, 4, 2, true),
+    WS_ENTRY_V(64, 56, 80, 128, 4, 2, false),
+    WS_ENTRY_V(32, 28, 96, 128, 4, 2, false),
 };
 
 }  // namespace
