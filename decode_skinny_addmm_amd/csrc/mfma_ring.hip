@@ -517,7 +517,8 @@ int64_t ring_max_k() { return INT64_MAX; }
     }
 
 // Public knobs of the wave-specialised form: path SKINNY_PATH_GEMM_WS, block_size = 512 (4
-// loader and 4 compute waves), outputs_per_block = BN, k_unroll = NS, vector_width = 8 (every
+// loader and 4 compute waves), outputs_per_block = BNV (the W rows a block owns: BN, or 7/8 of
+// it, 28 of a 32-row or 56 of a 64-row matrix tile), k_unroll = NS, vector_width = 8 (every
 // loader takes W and X rows) or 9 (W rows and X rows on different loaders), m_tile = BM,
 // k_split = WK (compute waves taking alternate K steps of a stage; the others split the block,
 // two along W rows), k_stage = KC (64, 128 or 256: 128-, 256- or 512-byte row pieces).

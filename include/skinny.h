@@ -80,7 +80,9 @@ enum {
                                  4 waves only load the stages, 4 only run the matrix
                                  instructions (block_size 512); k_split = compute waves taking
                                  alternate K steps; vector_width 8 = each loading wave takes W
-                                 and X rows, 9 = W rows and X rows on different waves; K must be
+                                 and X rows, 9 = W rows and X rows on different waves;
+                                 outputs_per_block 28 or 56 = blocks owning 7/8 of a 32- or
+                                 64-row matrix tile (256 or 128 blocks at N = 7168); K must be
                                  a multiple of k_stage (else SKINNY_ENOTSUP) */
 };
 
