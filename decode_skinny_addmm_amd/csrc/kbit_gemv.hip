@@ -157,7 +157,7 @@ __device__ __forceinline__ void block_dot_pair(const uint32_t (&P)[KB], uint32_t
 }
 
 // k = 3 and 4: the same pairs (e, e + 4) from a transposed block. A 4 x 4 bit-block transpose
-// of the plane words (two rounds of bit-field swaps between word pairs) leaves in word c, nibble
+// of the plane words (two passes of bit-field swaps between word pairs) leaves in word c, nibble
 // g, the index of element 4g + c (bit i from plane i; at k = 3 the fourth plane is zero), so
 // byte b of word c is index(8b + c) + 16 index(8b + c + 4): the pair table's entry number as it
 // stands. Its byte address is that byte times 8, one instruction (a byte-select shift) per
@@ -171,10 +171,10 @@ __device__ __forceinline__ void block_dot_tr(const uint32_t (&P)[KB], uint32_t a
     static_assert(KB == 3 || KB == 4, "four planes at most");
     auto bfi = [](uint32_t m, uint32_t v, uint32_t w) { return (m & v) | (~m & w); };
     uint32_t w0 = P[0], w1 = P[1], w2 = P[2], w3 = KB == 4 ? P[KB - 1] : zero;
-    // round 1: bits 4g + 2, 4g + 3 of words 0, 1 <-> bits 4g, 4g + 1 of words 2, 3
+    // first swap: bits 4g + 2, 4g + 3 of words 0, 1 <-> bits 4g, 4g + 1 of words 2, 3
     uint32_t n0 = bfi(0xCCCCCCCCu, w2 << 2, w0), n2 = bfi(0x33333333u, w0 >> 2, w2);
     uint32_t n1 = bfi(0xCCCCCCCCu, w3 << 2, w1), n3 = bfi(0x33333333u, w1 >> 2, w3);
-    // round 2: bits 4g + 1, 4g + 3 of words 0, 2 <-> bits 4g, 4g + 2 of words 1, 3
+    // second swap: bits 4g + 1, 4g + 3 of words 0, 2 <-> bits 4g, 4g + 2 of words 1, 3
     const uint32_t W[4] = {bfi(0xAAAAAAAAu, n1 << 1, n0), bfi(0x55555555u, n0 >> 1, n1),
                            bfi(0xAAAAAAAAu, n3 << 1, n2), bfi(0x55555555u, n2 >> 1, n3)};
     float s[MT];
