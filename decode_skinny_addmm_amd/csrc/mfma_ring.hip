@@ -24,7 +24,8 @@
 //   * R is fetched into registers before the K loop; the epilogue stages the block in LDS,
 //     adds the K-step groups in wave order and R in fp32, rounds once to bf16 and writes Y
 //     row-contiguously;
-//   * blocks are ordered so the m-tiles sharing one W tile run consecutively on one XCD.
+//   * blocks are ordered so that each XCD takes a contiguous run of n-tiles and the m-tiles
+//     sharing one W tile run consecutively on it.
 // A second kernel below runs the same ring with the waves split into loaders and compute waves.
 // K must be a multiple of KC.
 #include "common.hpp"
@@ -112,12 +113,15 @@ __global__ __launch_bounds__(NW * 64) void mfma_ring_kernel(const uint16_t *__re
     static_assert(PW * (NS - 2) < 64 && NS >= 2, "vmcnt budget");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
-    // block order: block b runs on XCD b % 8; consecutive blocks of one XCD take the m-tiles
-    // of one n-tile
+    // block order: block b runs on XCD b % 8; each XCD takes a contiguous run of n-tiles, and
+    // its consecutive blocks take the m-tiles of one n-tile. Neighbouring n-tiles then share
+    // their XCD's L2, so the 128-byte lines of R and Y that two blocks split (blocks of 32 or 28
+    // columns) are fetched once and written back whole (M = 16 9.73 -> 9.49 us, 64 14.13 ->
+    // 13.81 against n-tiles dealt round-robin over the XCDs)
     const int b = blockIdx.x;
     const int xcd = b & 7, j = b >> 3;
     const int mt = j % m_tiles;
-    const int nt = (j / m_tiles) * 8 + xcd;
+    const int nt = xcd * ((n_tiles + 7) / 8) + j / m_tiles;
     if (nt >= n_tiles) return;                       // padding block (uniform)
     const int n0 = nt * BN, m0 = mt * BM;
 
@@ -387,7 +391,7 @@ __global__ __launch_bounds__((NL + WK * WN * WM) * 64) void mfma_ring_ws_kernel(
     const int b = blockIdx.x;
     const int xcd = b & 7, j = b >> 3;
     const int mt = j % m_tiles;
-    const int nt = (j / m_tiles) * 8 + xcd;
+    const int nt = xcd * ((n_tiles + 7) / 8) + j / m_tiles;
     if (nt >= n_tiles) return;                       // padding block (uniform)
     const int n0 = nt * BNV, m0 = mt * BM;
 

@@ -27,8 +27,8 @@ ACC_FLOOR = 0.1
 # M values at which the GPU tests compare every output of the full N = 7168, K = 3584 problem
 # with the oracle at the selected configuration; together they reach every configuration the
 # table selects there for M = 1 ... 300 (checked on the CPU in test_abi_host.py).
-FULL_ORACLE_SMALL_M = [1, 2, 3, 4, 8, 9, 16]
-FULL_ORACLE_LARGE_M = [17, 26, 32, 33, 40, 41, 48, 49, 57, 64, 65, 80, 81, 88, 96, 97, 128, 129, 152, 160, 192, 208, 256]
+FULL_ORACLE_SMALL_M = [1, 2, 3, 4, 5, 8, 9, 16]
+FULL_ORACLE_LARGE_M = [17, 26, 32, 33, 40, 41, 48, 49, 57, 64, 65, 80, 81, 88, 96, 97, 128, 129, 152, 160, 176, 192, 208, 256]
 
 
 def bits_of(t: torch.Tensor) -> np.ndarray:
