@@ -117,6 +117,15 @@ __device__ __forceinline__ void store_output(void *out, const Epilogue &ep, int 
     }
 }
 
+// Block b of a 1-D grid of G blocks runs on XCD b % 8. xcd_run maps it to a contiguous run of
+// indices per XCD (a bijection of 0 .. G-1: XCD x takes G / 8 indices, one more when x < G % 8),
+// so blocks of neighbouring rows of W share an L2 and the 128-byte lines of R and Y that they
+// split are fetched once and written back whole.
+__device__ __forceinline__ int xcd_run(int b, int G) {
+    const int x = b & 7, q = G >> 3, r = G & 7;
+    return x * q + min(x, r) + (b >> 3);
+}
+
 // ---- cross-lane exchange steps (gfx950) ------------------------------------------------
 // pair_step<D>(x, y): lanes whose lane-id bit D is clear return x + (x of their partner),
 // lanes with the bit set return y + (y of their partner); partners differ exactly in bit D

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(KS * 64) void gemv_kernel(const uint16_t *__restric
     const int lane = threadIdx.x & 63;
     const int ks = threadIdx.x >> 6;
     const int G = gridDim.x;
-    const int g = blockIdx.x;
+    const int g = xcd_run(blockIdx.x, gridDim.x);  // contiguous row groups per XCD
     const int m0 = blockIdx.y * MT;
     const int NV = K >> 3;                      // 16-byte vectors per row
     const u32x4_t *Wv = reinterpret_cast<const u32x4_t *>(W);

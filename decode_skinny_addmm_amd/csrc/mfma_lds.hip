@@ -53,7 +53,7 @@ __global__ __launch_bounds__(KS * 64) void mfma_lds_kernel(const uint16_t *__res
     const int lane = tid & 63;
     const int ks = tid >> 6;
     const int G = gridDim.x;
-    const int g = blockIdx.x;
+    const int g = xcd_run(blockIdx.x, gridDim.x);  // contiguous row groups per XCD
     const int m0 = blockIdx.y * 16 * CT;
     const int NV = K >> 3;
     const u32x4_t *Wv = reinterpret_cast<const u32x4_t *>(W);
